@@ -1,0 +1,189 @@
+"""Pins of the oracle's verify (S5, S6).
+
+Pins: check (2) at T = 0 the output equals an independent autoregressive
+greedy decode of the target rows; check (3) chi-square tests at tiny vocab
+that every emitted token, conditional on its position being reached, follows
+the target distribution p; the closed-form acceptance probability
+sum_b min(p(b), q(b)); q = p always accepts; the residual draw has the same
+law for any chunk size; the degenerate-residual fallback samples p.
+"""
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import synth
+from oracle import dflash
+
+
+def _greedy_decode(Z, draft):
+    """Autoregressive greedy reference written independently of the oracle."""
+    L = len(draft)
+    out = []
+    for t in range(L + 1):
+        best = sorted(range(Z.shape[1]), key=lambda i: (-Z[t, i], i))[0]
+        out.append(best)
+        if t == L or draft[t] != best:
+            return len(out) - 1, out
+    raise AssertionError
+
+
+@pytest.mark.parametrize("set_id", range(6))
+def test_greedy_verify_is_longest_matching_run(set_id):
+    rng = np.random.default_rng(set_id)
+    L, V, K = 5, 40, 4
+    Z = np.round(rng.standard_normal((L + 1, V)) * 2) / 2      # ties included
+    cand = np.stack([rng.permutation(V)[:K] for _ in range(L)])
+    # make the drafts agree with the target for a random number of positions
+    agree = int(rng.integers(0, L + 1))
+    path = rng.integers(0, K, size=L)
+    for t in range(agree):
+        a = int(sorted(range(V), key=lambda i: (-Z[t, i], i))[0])
+        row = [int(c) for c in cand[t]]
+        if a in row:
+            path[t] = row.index(a)
+        else:
+            cand[t, path[t]] = a
+    q = np.eye(K)[path]
+    n, out, _ = dflash.verify_stream(Z, cand, path, q, 0.0, 1, 0)
+    n_ref, out_ref = _greedy_decode(Z, cand[np.arange(L), path])
+    assert n == n_ref
+    assert list(out[: n + 1]) == out_ref
+    assert np.all(out[n + 1:] == -1)
+
+
+def test_greedy_full_cycle_matches_decode():
+    inp = synth.make(1, set_id=2)
+    res = dflash.cycle_stream(inp, 0)
+    Z = dflash.widen(inp["Z"][0], "f32")
+    n_ref, out_ref = _greedy_decode(Z, res["draft_tok"])
+    assert res["accept_len"] == n_ref and list(res["out_tok"][: n_ref + 1]) == out_ref
+
+
+# ---------------------------------------------------------------- check (3)
+
+def _tiny_stream(rng, L, V, K):
+    Z = rng.standard_normal((L + 1, V)) * 1.5
+    S = rng.standard_normal((L, K, K))
+    S[0] = S[0][0][None, :]
+    cand = np.stack([rng.permutation(V)[:K] for _ in range(L)])
+    return Z, S, cand
+
+
+def _emitted_by_position(Z, S, cand, T, n_cycles, seed, chunk):
+    L = S.shape[0]
+    emitted = [[] for _ in range(L + 1)]
+    accepted_first = 0
+    for c in range(n_cycles):
+        path, draft, q, _ = dflash.trace_stream(S, cand, T, seed, c)
+        n, out, _ = dflash.verify_stream(Z, cand, path, q, T, seed, c, chunk=chunk)
+        for t in range(n + 1):
+            emitted[t].append(int(out[t]))
+        accepted_first += n >= 1
+    return emitted, accepted_first
+
+
+def _chi2_pvalue(tokens, p):
+    counts = np.bincount(tokens, minlength=p.size).astype(float)
+    exp = p * len(tokens)
+    keep = exp >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    ex = np.append(exp[keep], exp[~keep].sum())
+    if ex[-1] < 1e-9:
+        obs, ex = obs[:-1], ex[:-1]
+    return stats.chisquare(obs, ex).pvalue
+
+
+@pytest.mark.parametrize("V,K,L,T,chunk", [
+    (8, 2, 2, 1.0, 4096),
+    (16, 4, 2, 0.7, 3),
+    (12, 12, 1, 1.0, 1),
+    (64, 16, 2, 1.3, 16),
+])
+def test_emitted_tokens_follow_target(V, K, L, T, chunk):
+    rng = np.random.default_rng(V * 100 + K)
+    Z, S, cand = _tiny_stream(rng, L, V, K)
+    n_cycles = 6000
+    emitted, _ = _emitted_by_position(Z, S, cand, T, n_cycles, 0x1234 + V, chunk)
+    for t in range(L + 1):
+        if len(emitted[t]) < 200:
+            continue
+        p = special.softmax(Z[t] / T)
+        assert _chi2_pvalue(np.array(emitted[t]), p) > 1e-4, f"position {t + 1}"
+
+
+def test_first_position_acceptance_closed_form():
+    rng = np.random.default_rng(77)
+    V, K, L, T = 10, 3, 1, 1.0
+    Z, S, cand = _tiny_stream(rng, L, V, K)
+    n_cycles = 8000
+    _, acc = _emitted_by_position(Z, S, cand, T, n_cycles, 4242, 4096)
+    p = special.softmax(Z[0] / T)
+    q_full = np.zeros(V)
+    q_full[cand[0]] = special.softmax(S[0, 0] / T)
+    want = np.minimum(p, q_full).sum()
+    assert stats.binomtest(acc, n_cycles, want).pvalue > 1e-4
+
+
+def test_q_equal_p_always_accepts_and_bonus_follows_last_row():
+    rng = np.random.default_rng(5)
+    V, L, T = 6, 2, 0.9
+    Z = rng.standard_normal((L + 1, V))
+    cand = np.stack([rng.permutation(V) for _ in range(L)])       # K = V
+    S = np.stack([np.tile(Z[t, cand[t]], (V, 1)) for t in range(L)])
+    bonus = []
+    for c in range(3000):
+        path, draft, q, _ = dflash.trace_stream(S, cand, T, 9, c)
+        n, out, _ = dflash.verify_stream(Z, cand, path, q, T, 9, c)
+        assert n == L
+        bonus.append(int(out[L]))
+    assert _chi2_pvalue(np.array(bonus), special.softmax(Z[L] / T)) > 1e-4
+
+
+def test_residual_law_is_independent_of_chunk_size():
+    # the two-level draw over (chunks, candidates) has the law of the
+    # normalised residual for every chunk size; compare the residual draw
+    # alone by forcing a rejection at position 1 (q(d) >> p(d))
+    rng = np.random.default_rng(8)
+    V, K, T = 20, 4, 1.0
+    Z = rng.standard_normal((2, V))
+    cand = rng.permutation(V)[:K][None, :]
+    p = special.softmax(Z[0] / T)
+    q = np.zeros((1, K))
+    q[0] = [0.7, 0.1, 0.1, 0.1]
+    resid = p.copy()
+    resid[cand[0]] = np.maximum(0.0, p[cand[0]] - q[0])
+    resid /= resid.sum()
+    d_rank = np.array([int(np.argmax(q[0] - p[cand[0]]))])
+    for chunk in (1, 6, 4096):
+        toks = []
+        for c in range(4000):
+            n, out, _ = dflash.verify_stream(Z, cand, d_rank, q, T, 31, c, chunk=chunk)
+            if n == 0:
+                toks.append(int(out[0]))
+        assert len(toks) > 1000
+        assert _chi2_pvalue(np.array(toks), resid) > 1e-4, f"chunk {chunk}"
+
+
+def test_degenerate_residual_falls_back_to_p():
+    # q >= p on every candidate and no non-candidate mass (K = V): the
+    # residual is identically zero, so the draw must come from p itself
+    rng = np.random.default_rng(12)
+    V, T = 5, 1.0
+    Z = rng.standard_normal((2, V))
+    cand = np.arange(V)[None, :]
+    p = special.softmax(Z[0] / T)
+    q = (2.0 * p)[None, :]
+    toks = []
+    for c in range(5000):
+        n, out, _ = dflash.verify_stream(Z, cand, np.array([0]), q, T, 2, c)
+        if n == 0:
+            toks.append(int(out[0]))
+    assert len(toks) > 1000
+    assert _chi2_pvalue(np.array(toks), p) > 1e-4
+
+
+def test_rejects_negative_temperature():
+    with pytest.raises(ValueError):
+        dflash.verify_stream(np.zeros((2, 4)), np.array([[0, 1]]), np.array([0]),
+                             np.array([[1.0, 0.0]]), -1.0, 0, 0)
