@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash 2 draft -> select -> verify cycle on one MI355X.
+
+One step = one dflash_cycle call (top-K over the drafter rows, gate, pair
+scores, trace, target-row statistics and verify) for a whole batch of
+streams, with every input already resident in HBM.  Input sets rotate so
+that the timed working set exceeds twice the 256 MB last-level cache.
+
+Prints one JSON line (see README of the measurement in the design doc):
+  value      draft-verify cycles/s on one GPU
+  roofline   achieved algorithmic GB/s of the dominant kernel vs 8 TB/s
+  cpu_baseline  the float64 NumPy oracle on a bounded sample, host cores
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft-verify cycles/s + logit HBM GB/s (% of peak) at B=32, L=8, V=151936"
+HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 << 20
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "block_draft_select_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def logit_bytes(inp):
+    s = 2 if inp["logit_kind"] == "bf16" else 4
+    u = inp["B"] * inp["L"] * inp["V"] * s
+    z = inp["B"] * (inp["L"] + 1) * inp["V"] * s
+    return u, z
+
+
+def workload_name(inp):
+    Ts = sorted(set(float(t) for t in inp["T"]))
+    return (f"{inp['name']}: B={inp['B']} L={inp['L']} V={inp['V']} K={inp['K']} r={inp['r']} "
+            f"hidden={inp['hidden']} logits={inp['logit_kind']} params={inp['param_kind']} T={Ts}")
+
+
+def cpu_baseline(inp, seconds):
+    """The oracle as it stands, single-threaded, on a bounded sample of streams."""
+    import threadpoolctl
+    from oracle import dflash as O
+    done, t0 = 0, time.perf_counter()
+    with threadpoolctl.threadpool_limits(1):
+        while done < inp["B"] and (time.perf_counter() - t0) < seconds:
+            O.cycle_stream(inp, done)
+            done += 1
+    el = time.perf_counter() - t0
+    per_cycle = el / done * inp["B"]
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / per_cycle, "unit": "cycles/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {inp['B']} streams of input set 0 ({el:.1f} s), scaled to one "
+                      f"{inp['B']}-stream cycle",
+            "host_cpu": cpu, "host_cpu_count": os.cpu_count(),
+            "host_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def load_traffic(kernel):
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="input configuration id (1..5)")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for 2x LLC)")
+    ap.add_argument("--profile-steps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+                 "(the batch of streams shards by stream across GPUs with no exchange; see DESIGN.md)")
+
+    import torch
+    import synth
+    import block_draft_select_amd as dfl
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import alloc_outputs, device_inputs, dims_of
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    base = synth.make(args.config, set_id=0)
+    ub, zb = logit_bytes(base)
+    n_sets = args.sets or max(1, min(64, -(-2 * LLC_BYTES // (ub + zb))))
+    sets = [base] + [synth.make(args.config, set_id=s, plant=None) for s in range(1, n_sets)]
+    devs = [device_inputs(s) for s in sets]
+    _log(f"[bench] {workload_name(base)}; {n_sets} input sets generated in {time.perf_counter() - t_gen:.1f} s")
+
+    d = dims_of(base)
+    ws = dfl.workspace(d)
+    out = alloc_outputs(base)
+
+    def step(i):
+        dv = devs[i % n_sets]
+        dfl.dflash_cycle(d, dv["U"], dv["Z"], dv["x0"], dv["E"], dv["W"], dv["h"], dv["T"], dv["seed"], i,
+                         out["accept_len"], out["out_tok"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    _log(f"[bench] warmup {args.warmup} done")
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    cycles_per_s = args.steps / elapsed
+    mean_accept = float(out["accept_len"].float().mean().item())
+    _log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/cycle")
+
+    # per-kernel durations: HIP events recorded by the library around each
+    # launch on the stream it launches on
+    dfl.dflash_profile_enable(True)
+    for i in range(args.profile_steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in dfl.KERNELS:
+        n, ms = dfl.dflash_profile_collect(name)
+        if n:
+            kern[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+    dfl.dflash_profile_enable(False)
+    _log("[bench] kernels " + ", ".join(f"{k}={v['avg_us']:.1f}us" for k, v in kern.items()))
+
+    algo = {"topk": ub, "stats": zb}
+    dom = max(algo, key=lambda k: kern.get(k, {}).get("avg_us", 0.0))
+    achieved = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(dom),
+            "algorithmic_bytes_per_launch": algo[dom]}
+    per_kernel_roof = {k: round(algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1) for k in algo if k in kern}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(base, args.cpu_seconds)
+        _log(f"[bench] cpu baseline {cpu['value']:.4f} cycles/s")
+
+    logit_gbps = (ub + zb) / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(cycles_per_s, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload_name(base), "B": base["B"], "L": base["L"], "V": base["V"],
+                   "K": base["K"], "r": base["r"], "hidden": base["hidden"], "input_sets": n_sets},
+        "logit_GBps": round(logit_gbps, 1),
+        "logit_frac_of_peak": round(logit_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "kernel_GBps": per_kernel_roof,
+        "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "mean_accept_len": round(mean_accept, 3),
+        "cpu_baseline": cpu,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

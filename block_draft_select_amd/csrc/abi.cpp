@@ -1,0 +1,390 @@
+// C ABI of libdflash.so: host-side validation, workspace layout and the
+// launch sequence of every entry point declared in include/dflash.h.
+// Nothing here allocates device memory; all work goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dflash.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t logit_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
+
+dflash_status check_dims(const dflash_dims* d) {
+  if (!d) return fail(DFLASH_ERR_INVALID_ARG, "dims is NULL");
+  if (d->B < 1) return fail(DFLASH_ERR_INVALID_ARG, "B must be >= 1");
+  if (d->L < 1 || d->L > DFLASH_L_MAX) return fail(DFLASH_ERR_INVALID_ARG, "L must be in [1, 16]");
+  if (d->K < 1 || d->K > DFLASH_K_MAX) return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, 16]");
+  if (d->V < d->K) return fail(DFLASH_ERR_INVALID_ARG, "V must be >= K");
+  if (d->V > DFLASH_V_MAX) return fail(DFLASH_ERR_UNSUPPORTED, "V above DFLASH_V_MAX");
+  if (d->r < 16 || d->r > DFLASH_R_MAX || d->r % 16) return fail(DFLASH_ERR_INVALID_ARG, "r must be a multiple of 16 in [16, 256]");
+  if (d->hidden < 16 || d->hidden % 16) return fail(DFLASH_ERR_INVALID_ARG, "hidden must be a positive multiple of 16");
+  if (d->logit_dtype != DFLASH_F32 && d->logit_dtype != DFLASH_BF16) return fail(DFLASH_ERR_INVALID_ARG, "unknown logit_dtype");
+  if (d->param_dtype != DFLASH_F32 && d->param_dtype != DFLASH_BF16) return fail(DFLASH_ERR_INVALID_ARG, "unknown param_dtype");
+  if (((size_t)d->V * logit_bytes(d->logit_dtype)) % 16)
+    return fail(DFLASH_ERR_UNSUPPORTED, "a logit row must span a multiple of 16 bytes (V % 8 for bf16, V % 4 for fp32)");
+  const long long n_seg = (d->V + dfk::topk_block_elems(d->logit_dtype) - 1) / dfk::topk_block_elems(d->logit_dtype);
+  if (n_seg * 16 > dfk::kTopkMergeMax)
+    return fail(DFLASH_ERR_UNSUPPORTED, "V too large for the top-K merge (fp32 logits: V <= 1048576)");
+  const long long rows = (long long)d->B * (d->L + 1);
+  if (rows * ((d->V + DFLASH_CHUNK - 1) / DFLASH_CHUNK) > (1ll << 33) || (long long)d->B * d->L > (1ll << 30))
+    return fail(DFLASH_ERR_UNSUPPORTED, "problem too large for one launch");
+  return DFLASH_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Ptr {
+  const void* p;
+  const char* name;
+  bool need16;
+};
+
+dflash_status check_ptrs(std::initializer_list<Ptr> ps) {
+  for (const Ptr& p : ps) {
+    if (!p.p) return fail(DFLASH_ERR_INVALID_ARG, std::string(p.name) + " is NULL");
+    if (p.need16 && !aligned16(p.p)) return fail(DFLASH_ERR_INVALID_ARG, std::string(p.name) + " is not 16-byte aligned");
+  }
+  return DFLASH_OK;
+}
+
+dflash_status check_ws(const dfk::WsLayout& w, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(ws)) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < w.total)
+    return fail(DFLASH_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) + " bytes");
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------- timer
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[DFLASH_KERNEL_COUNT];
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Profiler& prof() {
+  static Profiler* p = new Profiler();
+  return *p;
+}
+
+// launch `f` on `st`, bracketed by events when the timer is on
+template <class F>
+hipError_t timed(int kernel, hipStream_t st, F f) {
+  Profiler& P = prof();
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (P.on) {
+      a = P.take();
+      b = P.take();
+    }
+  }
+  if (a) hipEventRecord(a, st);
+  const hipError_t e = f();
+  if (a && b) {
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.pending[kernel].push_back({a, b});
+  }
+  return e;
+}
+
+dflash_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DFLASH_OK;
+  return fail(DFLASH_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+namespace dfk {
+
+WsLayout ws_layout(const dflash_dims& d) {
+  WsLayout w{};
+  const size_t R = (size_t)d.B * d.L;
+  const int be = topk_block_elems(d.logit_dtype);
+  w.n_seg = (d.V + be - 1) / be;
+  w.n_chunk = (d.V + kChunk - 1) / kChunk;
+  size_t o = 0;
+  w.topk_partial = o; o = align256(o + (w.n_seg > 1 ? R * w.n_seg * 16 * sizeof(uint64_t) : 0));
+  w.topk_counter = o; o = align256(o + R * sizeof(uint32_t));
+  w.gate = o;         o = align256(o + R * d.r * sizeof(float));
+  w.cand_idx = o;     o = align256(o + R * d.K * sizeof(int32_t));
+  w.cand_logit = o;   o = align256(o + R * d.K * sizeof(float));
+  w.S = o;            o = align256(o + R * d.K * d.K * sizeof(float));
+  w.path_rank = o;    o = align256(o + R * sizeof(int32_t));
+  w.draft_tok = o;    o = align256(o + R * sizeof(int32_t));
+  w.q = o;            o = align256(o + R * d.K * sizeof(float));
+  w.stats = o;        o = align256(o + (size_t)d.B * (d.L + 1) * w.n_chunk * sizeof(ChunkStat));
+  w.total = o;
+  return w;
+}
+
+}  // namespace dfk
+
+extern "C" {
+
+int32_t dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "DFLASH_OK";
+    case DFLASH_ERR_INVALID_ARG: return "DFLASH_ERR_INVALID_ARG";
+    case DFLASH_ERR_UNSUPPORTED: return "DFLASH_ERR_UNSUPPORTED";
+    case DFLASH_ERR_WORKSPACE: return "DFLASH_ERR_WORKSPACE";
+    case DFLASH_ERR_HIP: return "DFLASH_ERR_HIP";
+    default: return "DFLASH_ERR_UNKNOWN";
+  }
+}
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+dflash_status dflash_workspace_bytes(const dflash_dims* d, size_t* bytes) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (!bytes) return fail(DFLASH_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = dfk::ws_layout(*d).total;
+    return DFLASH_OK;
+  } catch (...) {
+    return fail(DFLASH_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+dflash_status dflash_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(DFLASH_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    if (ws_bytes == 0) return DFLASH_OK;
+    return hip_status(dfk::launch_fill_zero(ws, ws_bytes, (hipStream_t)stream), "workspace fill");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_topk(const dflash_dims* d, const void* U, int32_t* cand_idx, float* cand_logit,
+                          void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{U, "U", true}, {cand_idx, "cand_idx", false}, {cand_logit, "cand_logit", false}})) return s;
+    const dfk::WsLayout w = dfk::ws_layout(*d);
+    if (dflash_status s = check_ws(w, ws, ws_bytes)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_TOPK, st, [&] {
+      return dfk::launch_topk(*d, w, U, cand_idx, cand_logit, static_cast<char*>(ws), st);
+    }), "topk launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_pair_scores(const dflash_dims* d, const int32_t* x0, const int32_t* cand_idx,
+                                 const float* cand_logit, const void* E, const void* W_g, const void* h,
+                                 float* S, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{x0, "x0", false}, {cand_idx, "cand_idx", false}, {cand_logit, "cand_logit", false},
+                                      {E, "E", true}, {W_g, "W_g", true}, {h, "h", true}, {S, "S", false}})) return s;
+    const dfk::WsLayout w = dfk::ws_layout(*d);
+    if (dflash_status s = check_ws(w, ws, ws_bytes)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    float* g = reinterpret_cast<float*>(static_cast<char*>(ws) + w.gate);
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_GATE, st, [&] { return dfk::launch_gate(*d, h, W_g, g, st); }), "gate launch")) return s;
+    return hip_status(timed(DFLASH_KERNEL_SCORES, st, [&] {
+      return dfk::launch_scores(*d, x0, cand_idx, cand_logit, E, g, S, st);
+    }), "scores launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_trace(const dflash_dims* d, const float* S, const int32_t* cand_idx, const float* T,
+                           const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
+                           float* q, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{S, "S", false}, {cand_idx, "cand_idx", false}, {T, "T", false}, {seed, "seed", false},
+                                      {path_rank, "path_rank", false}, {draft_tok, "draft_tok", false}, {q, "q", false}})) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_TRACE, st, [&] {
+      return dfk::launch_trace(*d, S, cand_idx, T, seed, cycle, path_rank, draft_tok, q, st);
+    }), "trace launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* cand_idx, const int32_t* path_rank,
+                            const float* q, const float* T, const uint64_t* seed, uint64_t cycle,
+                            int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{Z, "Z", true}, {cand_idx, "cand_idx", false}, {path_rank, "path_rank", false},
+                                      {q, "q", false}, {T, "T", false}, {seed, "seed", false},
+                                      {accept_len, "accept_len", false}, {out_tok, "out_tok", false}})) return s;
+    const dfk::WsLayout w = dfk::ws_layout(*d);
+    if (dflash_status s = check_ws(w, ws, ws_bytes)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    dfk::ChunkStat* stats = reinterpret_cast<dfk::ChunkStat*>(static_cast<char*>(ws) + w.stats);
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_STATS, st, [&] {
+          return dfk::launch_stats(*d, w, Z, cand_idx, T, stats, st);
+        }), "stats launch")) return s;
+    return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
+      return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
+    }), "finalize launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0, const void* E,
+                           const void* W_g, const void* h, const float* T, const uint64_t* seed, uint64_t cycle,
+                           int32_t* accept_len, int32_t* out_tok, int32_t* cand_idx_opt, float* cand_logit_opt,
+                           float* S_opt, int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{U, "U", true}, {Z, "Z", true}, {x0, "x0", false}, {E, "E", true},
+                                      {W_g, "W_g", true}, {h, "h", true}, {T, "T", false}, {seed, "seed", false},
+                                      {accept_len, "accept_len", false}, {out_tok, "out_tok", false}})) return s;
+    const dfk::WsLayout w = dfk::ws_layout(*d);
+    if (dflash_status s = check_ws(w, ws, ws_bytes)) return s;
+    char* base = static_cast<char*>(ws);
+    int32_t* cand_idx = cand_idx_opt ? cand_idx_opt : reinterpret_cast<int32_t*>(base + w.cand_idx);
+    float* cand_logit = cand_logit_opt ? cand_logit_opt : reinterpret_cast<float*>(base + w.cand_logit);
+    float* S = S_opt ? S_opt : reinterpret_cast<float*>(base + w.S);
+    int32_t* path_rank = path_rank_opt ? path_rank_opt : reinterpret_cast<int32_t*>(base + w.path_rank);
+    int32_t* draft_tok = draft_tok_opt ? draft_tok_opt : reinterpret_cast<int32_t*>(base + w.draft_tok);
+    float* q = q_opt ? q_opt : reinterpret_cast<float*>(base + w.q);
+    float* g = reinterpret_cast<float*>(base + w.gate);
+    dfk::ChunkStat* stats = reinterpret_cast<dfk::ChunkStat*>(base + w.stats);
+    hipStream_t st = (hipStream_t)stream;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TOPK, st, [&] {
+          return dfk::launch_topk(*d, w, U, cand_idx, cand_logit, base, st);
+        }), "topk launch")) return s;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_GATE, st, [&] { return dfk::launch_gate(*d, h, W_g, g, st); }), "gate launch")) return s;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_SCORES, st, [&] {
+          return dfk::launch_scores(*d, x0, cand_idx, cand_logit, E, g, S, st);
+        }), "scores launch")) return s;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TRACE, st, [&] {
+          return dfk::launch_trace(*d, S, cand_idx, T, seed, cycle, path_rank, draft_tok, q, st);
+        }), "trace launch")) return s;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_STATS, st, [&] {
+          return dfk::launch_stats(*d, w, Z, cand_idx, T, stats, st);
+        }), "stats launch")) return s;
+    return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
+      return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
+    }), "finalize launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_ptrs({{buf, "buf", true}, {sink, "sink", false}})) return s;
+    if (bytes % 16) return fail(DFLASH_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    return hip_status(dfk::launch_read_probe(buf, bytes, sink, (hipStream_t)stream), "read probe");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_ptrs({{dst, "dst", true}, {src, "src", true}})) return s;
+    if (bytes % 16) return fail(DFLASH_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    return hip_status(dfk::launch_copy_probe(dst, src, bytes, (hipStream_t)stream), "copy probe");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+const char* dflash_kernel_name(int32_t kernel) {
+  static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize"};
+  return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
+}
+
+dflash_status dflash_profile_enable(int32_t on) {
+  try {
+    g_err.clear();
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    for (auto& v : P.pending) {
+      for (auto& pr : v) {
+        hipEventSynchronize(pr.second);
+        P.pool.push_back(pr.first);
+        P.pool.push_back(pr.second);
+      }
+      v.clear();
+    }
+    P.on = on != 0;
+    return DFLASH_OK;
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_profile_collect(int32_t kernel, int64_t* launches, double* total_ms) {
+  try {
+    g_err.clear();
+    if (kernel < 0 || kernel >= DFLASH_KERNEL_COUNT) return fail(DFLASH_ERR_INVALID_ARG, "unknown kernel id");
+    if (!launches || !total_ms) return fail(DFLASH_ERR_INVALID_ARG, "output pointer is NULL");
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    double sum = 0.0;
+    int64_t n = 0;
+    for (auto& pr : P.pending[kernel]) {
+      if (hipEventSynchronize(pr.second) != hipSuccess) return fail(DFLASH_ERR_HIP, "event synchronize failed");
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return fail(DFLASH_ERR_HIP, "event timing failed");
+      sum += ms;
+      ++n;
+      P.pool.push_back(pr.first);
+      P.pool.push_back(pr.second);
+    }
+    P.pending[kernel].clear();
+    *launches = n;
+    *total_ms = sum;
+    return DFLASH_OK;
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+}  // extern "C"

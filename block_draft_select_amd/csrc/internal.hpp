@@ -1,0 +1,63 @@
+// Host-side declarations shared by the ABI layer and the kernel files:
+// geometry constants, the workspace layout and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dflash.h"
+
+namespace dfk {
+
+// top-K streaming geometry: a wave owns 8 16-byte loads per lane; a block of
+// 4 waves owns one segment of a drafter row
+constexpr int kTopkThreads = 256;
+constexpr int kTopkLoads = 8;
+constexpr int kTopkCap = 256;          // candidate buffer per wave
+constexpr int kTopkMergeMax = 2048;    // keys the last block of a row merges in LDS
+
+inline int topk_wave_elems(int logit_dtype) { return 64 * kTopkLoads * (logit_dtype == DFLASH_BF16 ? 8 : 4); }
+inline int topk_block_elems(int logit_dtype) { return 4 * topk_wave_elems(logit_dtype); }
+
+constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
+
+struct ChunkStat {
+  float m;      // chunk maximum logit
+  float s;      // sum over non-candidates of exp((z - m) / T)  (sampling rows)
+  int32_t arg;  // first index of the maximum (greedy rows)
+  int32_t pad;
+};
+
+struct WsLayout {
+  int n_seg;    // top-K segments per drafter row
+  int n_chunk;  // target chunks per row
+  size_t topk_partial, topk_counter, gate, cand_idx, cand_logit, S, path_rank, draft_tok, q, stats;
+  size_t total;
+};
+
+WsLayout ws_layout(const dflash_dims& d);
+
+// ---- launchers (each enqueues on `st`; returns the launch status) ----
+
+hipError_t launch_topk(const dflash_dims& d, const WsLayout& w, const void* U, int32_t* cand_idx,
+                       float* cand_logit, char* ws, hipStream_t st);
+hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* g, hipStream_t st);
+hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t* cand_idx,
+                         const float* cand_logit, const void* E, const float* g, float* S,
+                         hipStream_t st);
+hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
+                        const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
+                        float* q, hipStream_t st);
+hipError_t launch_stats(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
+                        const float* T, ChunkStat* stats, hipStream_t st);
+hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* Z,
+                           const int32_t* cand_idx, const int32_t* path_rank, const float* q,
+                           const float* T, const uint64_t* seed, uint64_t cycle,
+                           const ChunkStat* stats, int32_t* accept_len, int32_t* out_tok,
+                           hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+}  // namespace dfk

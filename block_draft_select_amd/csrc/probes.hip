@@ -1,0 +1,69 @@
+// Workspace fill and the two measurement kernels (plain streaming read and
+// plain copy) used to calibrate bandwidth figures and hardware counters.
+#include "device_util.hpp"
+#include "internal.hpp"
+
+namespace dfk {
+
+namespace {
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                                                        size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+}
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                         size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+unsigned grid_for(size_t n16) {
+  const size_t blocks = (n16 + 255) / 256;
+  const size_t cap = 256 * 32;  // 32 blocks per CU on 256 CUs
+  return (unsigned)(blocks < cap ? (blocks ? blocks : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n16,
+                     reinterpret_cast<uint8_t*>(p) + n16 * 16, bytes - n16 * 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(grid_for(n16)), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(buf), n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(dst),
+                     reinterpret_cast<const uint4*>(src), n16);
+  return hipGetLastError();
+}
+
+}  // namespace dfk

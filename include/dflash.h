@@ -1,0 +1,219 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash 2 draft -> select -> verify
+ * hot path.  Library: block_draft_select_amd/libdflash.so.
+ *
+ * The method (four web pages on DFlash 2, cited by title and section):
+ *   P1 "DFlash 2: Block diffusion, wearing a drafter's coat", section
+ *      "The architecture" (sub-sections "Sixteen candidates per position",
+ *      "A path selector", "Lossless, with conditions I did not used to state").
+ *   P2 "A 2B Drafter Made a 27B Model 3.4x Faster. Same Exact Output.",
+ *      sections "What a block-diffusion drafter is, and why it kept
+ *      breaking", "The two fixes", "Caveats before you rebuild your serving
+ *      stack".
+ *   P3 "DFlash 2: Keep Drafting Parallel" (news text), section "What Comes
+ *      Next", paragraph "A Lightweight Path Selector".
+ *
+ * One cycle of B independent streams: the drafter gives L logit rows U
+ * (one per drafted position) and L context vectors h; the library keeps the
+ * K best candidates per position, scores every adjacent candidate pair with
+ * the drafter logit plus a gated bilinear embedding match, walks one path
+ * through the candidate lattice, and verifies it against L+1 target logit
+ * rows Z by rejection sampling (accept with min(1, p/q), resample from the
+ * normalised residual max(0, p - q), bonus token when all L are accepted).
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains caller memory.  Arrays are
+ *     dense row-major with the shapes given in brackets.  U, Z, E, W_g and h
+ *     must be 16-byte aligned.
+ *   - Scratch lives in a caller-provided device workspace of at least
+ *     dflash_workspace_bytes() bytes, zero-filled before its first use
+ *     (dflash_workspace_init does that).  The library leaves its counters
+ *     at zero after every completed call, so the same workspace can be
+ *     reused by later calls on the same stream without clearing it again.
+ *     Calls that overlap in time must not share a workspace.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream).  Outputs are valid once the caller
+ *     synchronises with that stream.
+ *   - Arguments are validated on the host before anything is enqueued: an
+ *     invalid call returns an error status, launches nothing and leaves
+ *     every output untouched.  dflash_last_error() then gives a message
+ *     (thread-local).  No C++ exception crosses this boundary.
+ *   - Outputs are a pure function of the inputs (including seed[] and
+ *     cycle); they do not depend on launch shapes, split factors or timing.
+ *   - Device-side index inputs (x0, cand_idx, path_rank) that lie outside
+ *     their range are clamped into it, so no out-of-bounds access occurs;
+ *     the outputs of such a stream are then unspecified.
+ *   - Logits must be finite; NaN or infinite logits give unspecified
+ *     results.  A temperature T[b] > 0 selects sampling for stream b; any
+ *     other value (0, negative, NaN) selects greedy decoding.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+#define DFLASH_K_MAX 16      /* candidates kept per position */
+#define DFLASH_L_MAX 16      /* drafted positions per block */
+#define DFLASH_R_MAX 256     /* embedding rank */
+#define DFLASH_V_MAX 2097152 /* vocabulary size */
+#define DFLASH_CHUNK 4096    /* tokens per first-level item of the residual draw */
+
+typedef int32_t dflash_status;
+enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = 1, /* bad dimension, null or misaligned pointer */
+  DFLASH_ERR_UNSUPPORTED = 2, /* valid request this build does not handle */
+  DFLASH_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  DFLASH_ERR_HIP = 4          /* the HIP runtime refused a launch */
+};
+
+/* element type of U and Z (logit_dtype) and of E, W_g and h (param_dtype) */
+enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 };
+
+typedef struct dflash_dims {
+  int32_t B;           /* streams, >= 1 */
+  int32_t L;           /* drafted positions, 1..DFLASH_L_MAX */
+  int32_t V;           /* vocabulary, K..DFLASH_V_MAX; V * sizeof(logit) % 16 == 0 */
+  int32_t K;           /* candidates per position, 1..DFLASH_K_MAX */
+  int32_t r;           /* embedding rank, 16..DFLASH_R_MAX, multiple of 16 */
+  int32_t hidden;      /* context width, >= 16, multiple of 16 */
+  int32_t logit_dtype; /* DFLASH_F32 | DFLASH_BF16 */
+  int32_t param_dtype; /* DFLASH_F32 | DFLASH_BF16 */
+} dflash_dims;
+
+/* Version of this ABI (DFLASH_ABI_VERSION). */
+int32_t dflash_abi_version(void);
+
+/* Static name of a status code. */
+const char* dflash_status_string(dflash_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* dflash_last_error(void);
+
+/* Bytes of workspace every entry point needs for `d` (host only, pure).
+ * Returns DFLASH_ERR_INVALID_ARG / DFLASH_ERR_UNSUPPORTED for bad dims. */
+dflash_status dflash_workspace_bytes(const dflash_dims* d, size_t* bytes);
+
+/* Zero-fill `ws_bytes` bytes of a workspace on `stream` (a fill kernel). */
+dflash_status dflash_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* S1 -- top-K candidates per drafted position (P1 "Sixteen candidates per
+ * position"; P2 "What a block-diffusion drafter is ...").
+ *   U          [B, L, V] logits (logit_dtype)
+ *   cand_idx   [B, L, K] int32 out: token ids, ordered by logit descending,
+ *              equal logits by token id ascending (-0.0 equals +0.0)
+ *   cand_logit [B, L, K] float out: those logits, widened exactly to fp32 */
+dflash_status dflash_topk(const dflash_dims* d, const void* U, int32_t* cand_idx,
+                          float* cand_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* S2 + S3 -- context gate and adjacent pair scores (P3 "A Lightweight Path
+ * Selector"; P1 "A path selector").  With g_t = sigmoid(h_t @ W_g):
+ *   S[b,t,i,j] = cand_logit[b,t,j] + sum_k E[a_i,k] * g_t[k] * E[c_j,k]
+ * where c_j = cand_idx[b,t,j] and a_i = cand_idx[b,t-1,i] for t >= 1, and
+ * a_i = x0[b] (the last verified token) for every row i of edge t = 0.
+ *   x0         [B] int32, the last verified token of each stream
+ *   cand_idx   [B, L, K] int32, cand_logit [B, L, K] float (from dflash_topk)
+ *   E          [V, r] candidate embeddings (param_dtype)
+ *   W_g        [hidden, r] gate weights (param_dtype)
+ *   h          [B, L, hidden] drafter context (param_dtype)
+ *   S          [B, L, K, K] float out (rows: predecessor rank, cols: rank) */
+dflash_status dflash_pair_scores(const dflash_dims* d, const int32_t* x0,
+                                 const int32_t* cand_idx, const float* cand_logit,
+                                 const void* E, const void* W_g, const void* h, float* S,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* S4 -- walk one path through the lattice (P3 "A Lightweight Path Selector").
+ * Starting at rank 0 of edge 0, position t picks rank j_t from row j_{t-1}
+ * of S[b,t]: greedy (smallest rank attaining the maximum) when T[b] <= 0,
+ * otherwise a draw from q_t = softmax(S[b,t,j_{t-1},:] / T[b]) by inverse
+ * CDF with the fp32 uniform u = ((w >> 9) * 2 + 1) * 2^-24 of word 0 of
+ * Philox4x32-10(key = seed[b], counter = (cycle lo, cycle hi, t + 1, 0)).
+ *   T          [B] float temperatures;  seed [B] uint64 Philox keys
+ *   path_rank  [B, L] int32 out;  draft_tok [B, L] int32 out (the tokens)
+ *   q          [B, L, K] float out: q_t (one-hot at T <= 0) */
+dflash_status dflash_trace(const dflash_dims* d, const float* S, const int32_t* cand_idx,
+                           const float* T, const uint64_t* seed, uint64_t cycle,
+                           int32_t* path_rank, int32_t* draft_tok, float* q, void* stream);
+
+/* S5 + S6 -- verify against the target (P1 "Lossless, with conditions I did
+ * not used to state"; P2 "Caveats before you rebuild your serving stack").
+ * Greedy streams accept the longest prefix whose drafts equal the target
+ * argmax (smallest index on ties) and emit the argmax of the next row.
+ * Sampling streams accept position t while u_t * q_t(d_t) < p_t(d_t), with
+ * p_t = softmax(Z[b,t,:] / T[b]) and u_t the fp32 uniform of word 1 of the
+ * (cycle, t + 1, 0) block; at the first rejection (or after L accepts, on
+ * row L with no candidates) one token is drawn from the normalised residual
+ * (max(0, p - q) on the candidates of that position, p elsewhere; p itself
+ * if that residual has no mass) in two inverse-CDF levels: fp64 uniform u1
+ * (words 0,1 of the (cycle, row + 1, 1) block) picks an item among
+ * [DFLASH_CHUNK-token chunks carrying their non-candidate mass, then the K
+ * candidates]; u2 (words 2,3) picks the token inside a picked chunk; each
+ * fp64 uniform is ((hi:lo >> 12) * 2 + 1) * 2^-53.
+ *   Z          [B, L + 1, V] target logits (logit_dtype)
+ *   cand_idx   [B, L, K], path_rank [B, L], q [B, L, K] (from dflash_trace)
+ *   accept_len [B] int32 out: accepted drafts n in 0..L
+ *   out_tok    [B, L + 1] int32 out: the n accepted drafts, then the
+ *              resampled or bonus token, then -1 padding */
+dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* cand_idx,
+                            const int32_t* path_rank, const float* q, const float* T,
+                            const uint64_t* seed, uint64_t cycle, int32_t* accept_len,
+                            int32_t* out_tok, void* ws, size_t ws_bytes, void* stream);
+
+/* One whole cycle: dflash_topk, dflash_pair_scores, dflash_trace and
+ * dflash_verify on one stream, with identical results.  The intermediate
+ * outputs (cand_idx [B,L,K], cand_logit [B,L,K], S [B,L,K,K],
+ * path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written where the
+ * caller passes non-NULL pointers and kept in the workspace otherwise. */
+dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
+                           const int32_t* x0, const void* E, const void* W_g, const void* h,
+                           const float* T, const uint64_t* seed, uint64_t cycle,
+                           int32_t* accept_len, int32_t* out_tok,
+                           int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
+                           int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- measurement helpers (not part of the method) ---------------------- */
+
+/* Stream-read `bytes` (multiple of 16, 16-byte aligned) of `buf` and write
+ * a 32-bit checksum to *sink: the achievable HBM read ceiling. */
+dflash_status dflash_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/* Plain copy of `bytes` (multiple of 16, both 16-byte aligned): the
+ * reference kernel for scaling hardware byte counters. */
+dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Kernel identifiers for the per-kernel timer. */
+enum {
+  DFLASH_KERNEL_TOPK = 0,
+  DFLASH_KERNEL_GATE = 1,
+  DFLASH_KERNEL_SCORES = 2,
+  DFLASH_KERNEL_TRACE = 3,
+  DFLASH_KERNEL_STATS = 4,
+  DFLASH_KERNEL_FINALIZE = 5,
+  DFLASH_KERNEL_COUNT = 6
+};
+
+/* Name of a kernel identifier ("" if out of range). */
+const char* dflash_kernel_name(int32_t kernel);
+
+/* Enable (on != 0) or disable the per-kernel timer: while enabled, every
+ * launch is bracketed by hipEvents recorded on its own stream.  Enabling
+ * discards earlier samples.  Host-side state shared by all threads. */
+dflash_status dflash_profile_enable(int32_t on);
+
+/* Wait for recorded launches of `kernel` and return their count and summed
+ * duration in milliseconds; the samples are then discarded. */
+dflash_status dflash_profile_collect(int32_t kernel, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

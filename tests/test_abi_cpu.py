@@ -1,0 +1,92 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/dflash.h declares, and rejects invalid calls on the host before any
+HIP call (so these run on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dfl():
+    import block_draft_select_amd as m
+    return m
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(dfl):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(dfl.lib, n), n
+    # and the binding exposes a function of the same name for each entry point
+    for n in ("dflash_topk", "dflash_pair_scores", "dflash_trace", "dflash_verify", "dflash_cycle"):
+        assert callable(getattr(dfl, n))
+
+
+def test_version_and_strings(dfl):
+    assert dfl.lib.dflash_abi_version() == 1
+    assert dfl.lib.dflash_status_string(3) == b"DFLASH_ERR_WORKSPACE"
+    assert dfl.lib.dflash_kernel_name(0) == b"topk"
+    assert dfl.lib.dflash_kernel_name(99) == b""
+
+
+def test_workspace_bytes_of_the_five_configs(dfl):
+    import synth
+    for cid, cfg in synth.CONFIGS.items():
+        d = dfl.dims(cfg["B"], cfg["L"], cfg["V"], cfg["K"], cfg["r"], cfg["hidden"],
+                     cfg["logit_kind"], cfg["param_kind"])
+        n = dfl.workspace_bytes(d)
+        R = cfg["B"] * cfg["L"]
+        # the chunk statistics alone take B*(L+1)*ceil(V/4096)*16 bytes
+        assert n >= cfg["B"] * (cfg["L"] + 1) * (-(-cfg["V"] // 4096)) * 16
+        assert n >= R * cfg["r"] * 4
+        assert n < 64 << 20
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, 1), ("L", 0, 1), ("L", 17, 1), ("K", 0, 1), ("K", 17, 1), ("V", 8, 1),
+    ("V", 4 * 1024 * 1024, 2), ("r", 8, 1), ("r", 264, 1), ("r", 40, 1), ("hidden", 8, 1),
+    ("hidden", 100, 1), ("logit_dtype", 7, 1), ("param_dtype", -1, 1), ("V", 1001, 2),
+])
+def test_bad_dims_rejected(dfl, field, value, status):
+    d = dfl.dims(2, 8, 4096, 16, 256, 256, "bf16", "bf16")
+    setattr(d, field, value)
+    n = ctypes.c_size_t(12345)
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == status
+    assert n.value == 12345
+    assert dfl.lib.dflash_last_error() != b""
+    # every entry point refuses the same dims before touching any pointer
+    assert dfl.lib.dflash_topk(ctypes.byref(d), None, None, None, None, 0, None) == status
+    assert dfl.lib.dflash_cycle(ctypes.byref(d), *([None] * 8), 0, *([None] * 8), None, 0, None) == status
+
+
+def test_fp32_vocab_limit(dfl):
+    d = dfl.dims(1, 1, 1048576 + 4, 16, 16, 16, "f32", "f32")
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 2
+    d = dfl.dims(1, 1, 1048576, 16, 16, 16, "f32", "f32")
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 0
+
+
+def test_null_and_misaligned_pointers_rejected(dfl):
+    d = dfl.dims(1, 2, 4096, 4, 16, 16, "bf16", "bf16")
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    assert dfl.lib.dflash_topk(ctypes.byref(d), None, fake, fake, fake, 1 << 30, None) == 1
+    assert b"U is NULL" in dfl.lib.dflash_last_error()
+    assert dfl.lib.dflash_topk(ctypes.byref(d), odd, fake, fake, fake, 1 << 30, None) == 1
+    assert b"aligned" in dfl.lib.dflash_last_error()
+    # workspace checks come after pointer checks and still launch nothing
+    assert dfl.lib.dflash_topk(ctypes.byref(d), fake, fake, fake, None, 1 << 30, None) == 3
+    assert dfl.lib.dflash_topk(ctypes.byref(d), fake, fake, fake, fake, 16, None) == 3
+    assert b"too small" in dfl.lib.dflash_last_error()
+    assert dfl.lib.dflash_read_probe(fake, 17, fake, None) == 1
+    assert dfl.lib.dflash_profile_collect(42, None, None) == 1

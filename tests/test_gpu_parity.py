@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path against the float64 oracle, through the C ABI.
+
+Bar: bit-exact candidate indices and logits, selected paths, draft tokens,
+accept counts and emitted tokens; pair scores within 1e-4 relative (floor 1);
+q within 2e-6 absolute.  Inputs are seeded synthetic sets (``synth``) passed
+through the oracle's near-tie margin guard (``tests/guard.py``).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from guard import guarded
+from gpu_util import alloc_outputs, compare_stream, device_inputs, dims_of, run_cycle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_select_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+# (name, config id, overrides, guard the greedy trace gap)
+SMALL = [
+    ("tiny-f32-greedy", 1, dict(), True),
+    ("tiny-f32-sampling", 1, dict(B=3, T=0.8), True),
+    ("bf16-T1-ragged", 3, dict(B=4, V=20008, hidden=256), True),
+    ("bf16-T0-ragged", 2, dict(B=3, V=20008, hidden=256), True),
+    ("bf16-mixedT", 5, dict(B=6, V=12296, hidden=512), True),
+    ("bf16-strong-selector", 3, dict(B=4, V=9000, hidden=256, e_std=0.3), True),
+    ("bf16-strong-greedy", 2, dict(B=3, V=9000, hidden=256, e_std=0.3, T=0.0), True),
+    ("bf16-ties-T1", 3, dict(B=3, V=16392, hidden=256, ties=True), True),
+    ("bf16-ties-T0", 2, dict(B=3, V=16392, hidden=256, ties=True, T=0.0), True),
+    ("bf16-K4-L3", 3, dict(B=4, V=4096, hidden=256, K=4, L=3), True),
+    ("bf16-K1-L1", 3, dict(B=2, V=1000, hidden=256, K=1, L=1), True),
+    ("bf16-L16", 4, dict(B=2, V=20000, hidden=256), True),
+    ("bf16-r16-T06", 3, dict(B=3, V=8200, hidden=64, r=16, T=0.6), True),
+    ("bf16-single-chunk", 3, dict(B=5, V=64, K=16, hidden=256, plant=None), True),
+]
+
+
+@pytest.mark.parametrize("name,cid,kw,gt", SMALL, ids=[c[0] for c in SMALL])
+def test_cycle_matches_oracle_small(name, cid, kw, gt):
+    inp = synth.make(cid, set_id=101, **kw)
+    _say(f"[parity] {name}: B={inp['B']} L={inp['L']} V={inp['V']} K={inp['K']} r={inp['r']}")
+    ref, redraws = guarded(inp, guard_trace=gt)
+    gpu = run_cycle(inp)
+    for b in range(inp["B"]):
+        compare_stream(gpu, ref[b], b)
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_zero_embeddings_independent_top1(ties):
+    inp = synth.make(3, set_id=5, B=4, V=8192, hidden=256, zero_E=True, ties=ties, T=0.0)
+    _say(f"[parity] zero-E ties={ties}")
+    ref, _ = guarded(inp, guard_trace=False)
+    gpu = run_cycle(inp)
+    assert np.all(gpu["path_rank"] == 0)
+    for b in range(inp["B"]):
+        compare_stream(gpu, ref[b], b)
+
+
+FULL = [
+    ("C1", 1, None),
+    ("C2", 2, None),
+    ("C3", 3, [0, 13, 31]),
+    ("C4", 4, [0, 31]),
+    ("C5", 5, [0, 1, 2, 3, 127]),
+]
+
+
+@pytest.mark.parametrize("name,cid,streams", FULL, ids=[c[0] for c in FULL])
+def test_full_size_configs_sampled(name, cid, streams):
+    inp = synth.make(cid, set_id=0)
+    _say(f"[parity] full {name}: B={inp['B']} L={inp['L']} V={inp['V']} streams={streams}")
+    ref, redraws = guarded(inp, streams=streams)
+    gpu = run_cycle(inp)
+    for b in ref:
+        compare_stream(gpu, ref[b], b)
+
+
+def test_split_entry_points_equal_cycle():
+    import torch
+    import block_draft_select_amd as dfl
+    inp = synth.make(3, set_id=77, B=3, V=20008, hidden=256)
+    _say("[parity] split entry points vs dflash_cycle")
+    d = dims_of(inp)
+    dev = device_inputs(inp)
+    whole = run_cycle(inp, dev=dev)
+    o = alloc_outputs(inp)
+    ws = dfl.workspace(d)
+    dfl.dflash_topk(d, dev["U"], o["cand_idx"], o["cand_logit"], ws)
+    dfl.dflash_pair_scores(d, dev["x0"], o["cand_idx"], o["cand_logit"], dev["E"], dev["W"], dev["h"], o["S"], ws)
+    dfl.dflash_trace(d, o["S"], o["cand_idx"], dev["T"], dev["seed"], inp["cycle"], o["path_rank"],
+                     o["draft_tok"], o["q"])
+    dfl.dflash_verify(d, dev["Z"], o["cand_idx"], o["path_rank"], o["q"], dev["T"], dev["seed"], inp["cycle"],
+                      o["accept_len"], o["out_tok"], ws)
+    torch.cuda.synchronize()
+    for k, v in o.items():
+        np.testing.assert_array_equal(v.cpu().numpy(), whole[k], err_msg=k)
+
+
+def test_deterministic_and_workspace_reuse():
+    import block_draft_select_amd as dfl
+    a = synth.make(5, set_id=3, B=5, V=12296, hidden=256)
+    b = synth.make(5, set_id=4, B=5, V=12296, hidden=256)
+    _say("[parity] determinism + workspace reuse")
+    ref_a, _ = guarded(a)
+    ref_b, _ = guarded(b)
+    ws = dfl.workspace(dims_of(a))
+    r1 = run_cycle(a, ws=ws)
+    r2 = run_cycle(b, ws=ws)
+    r3 = run_cycle(a, ws=ws)
+    for k in r1:
+        np.testing.assert_array_equal(r1[k], r3[k], err_msg=k)
+    for s in range(a["B"]):
+        compare_stream(r1, ref_a[s], s)
+        compare_stream(r2, ref_b[s], s)
+
+
+def test_topk_alone_special_rows():
+    import torch
+    import block_draft_select_amd as dfl
+    from oracle import dflash as O
+    _say("[parity] topk special rows")
+    V, K, L = 16392, 16, 6
+    rng = np.random.default_rng(3)
+    rows = np.zeros((L, V), dtype=np.float32)
+    rows[0] = 1.5                                           # all equal: lowest 16 indices
+    rows[1] = -3.0
+    rows[1, 5000:5010] = -0.0                              # signed zeros among negatives
+    rows[1, 7000:7010] = 0.0
+    rows[2] = np.sort(rng.standard_normal(V))[::-1]         # descending: concentrated in few lanes
+    rows[3] = np.sort(rng.standard_normal(V))               # ascending: top at the ragged tail
+    rows[4] = np.round(rng.standard_normal(V) * 2) / 2      # heavy ties
+    rows[5] = rng.standard_normal(V) * 1e-3 - 50.0           # all negative
+    bits = synth.bf16_bits(rows)
+    inp = dict(B=1, L=L, V=V, K=K, r=16, hidden=16, logit_kind="bf16", param_kind="bf16")
+    d = dims_of(inp)
+    U = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ci = torch.empty((L, K), dtype=torch.int32, device="cuda")
+    cl = torch.empty((L, K), dtype=torch.float32, device="cuda")
+    dfl.dflash_topk(d, U, ci, cl, dfl.workspace(d))
+    torch.cuda.synchronize()
+    for t in range(L):
+        idx, val = O.topk_row(O.widen(bits[t], "bf16"), K)
+        np.testing.assert_array_equal(ci[t].cpu().numpy(), idx, err_msg=f"row {t}")
+        np.testing.assert_array_equal(cl[t].cpu().numpy().astype(np.float64), val, err_msg=f"row {t}")
+
+
+def test_invalid_calls_launch_nothing():
+    import torch
+    import block_draft_select_amd as dfl
+    _say("[parity] invalid calls")
+    inp = synth.make(3, set_id=1, B=2, V=4096, hidden=256)
+    d = dims_of(inp)
+    dev = device_inputs(inp)
+    o = alloc_outputs(inp)
+    small = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dfl.DFlashError) as e:
+        dfl.dflash_cycle(d, dev["U"], dev["Z"], dev["x0"], dev["E"], dev["W"], dev["h"], dev["T"], dev["seed"],
+                         0, o["accept_len"], o["out_tok"], small)
+    assert e.value.status == dfl.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(o["accept_len"] == -7) and torch.all(o["out_tok"] == -7)
