@@ -21,7 +21,8 @@ K_MAX, L_MAX, R_MAX, V_MAX, CHUNK = 16, 16, 256, 2097152, 4096
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
-KERNELS = ("topk", "gate", "scores", "trace", "stats", "finalize")
+KERNELS = ("topk", "gate", "scores", "trace", "stats", "finalize", "cycle_stream", "cycle_scores",
+           "cycle_finalize")
 
 
 class dflash_dims(ctypes.Structure):

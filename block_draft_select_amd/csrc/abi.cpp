@@ -3,6 +3,7 @@
 // Nothing here allocates device memory; all work goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <string>
@@ -37,12 +38,8 @@ dflash_status check_dims(const dflash_dims* d) {
   if (d->param_dtype != DFLASH_F32 && d->param_dtype != DFLASH_BF16) return fail(DFLASH_ERR_INVALID_ARG, "unknown param_dtype");
   if (((size_t)d->V * logit_bytes(d->logit_dtype)) % 16)
     return fail(DFLASH_ERR_UNSUPPORTED, "a logit row must span a multiple of 16 bytes (V % 8 for bf16, V % 4 for fp32)");
-  const long long n_seg = (d->V + dfk::topk_block_elems(d->logit_dtype) - 1) / dfk::topk_block_elems(d->logit_dtype);
-  if (n_seg * 16 > dfk::kTopkMergeMax)
-    return fail(DFLASH_ERR_UNSUPPORTED, "V too large for the top-K merge (fp32 logits: V <= 1048576)");
   const long long rows = (long long)d->B * (d->L + 1);
-  if (rows * ((d->V + DFLASH_CHUNK - 1) / DFLASH_CHUNK) > (1ll << 33) || (long long)d->B * d->L > (1ll << 30))
-    return fail(DFLASH_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (rows > 65535) return fail(DFLASH_ERR_UNSUPPORTED, "B * (L + 1) must not exceed 65535");
   return DFLASH_OK;
 }
 
@@ -126,18 +123,39 @@ dflash_status hip_status(hipError_t e, const char* what) {
 
 namespace dfk {
 
+// Sub-segments per top-K block: by default the smallest multiple of 4 that
+// keeps the top-K part of the grid at or below 2048 blocks; at least enough
+// that a row has at most kTopkMaxSeg blocks.  DFLASH_TOPK_SPB overrides the
+// default for tuning sweeps.
+static int topk_spb(size_t rows, int n_sub) {
+  static const int env = [] {
+    const char* s = std::getenv("DFLASH_TOPK_SPB");
+    return s ? std::atoi(s) : 0;
+  }();
+  int spb = 4;
+  if (env > 0) {
+    spb = env;
+  } else {
+    while (spb < n_sub && rows * (size_t)((n_sub + spb - 1) / spb) > 2048) spb += 4;
+  }
+  const int min_spb = (n_sub + kTopkMaxSeg - 1) / kTopkMaxSeg;
+  return spb < min_spb ? min_spb : spb;
+}
+
 WsLayout ws_layout(const dflash_dims& d) {
   WsLayout w{};
   const size_t R = (size_t)d.B * d.L;
-  const int be = topk_block_elems(d.logit_dtype);
-  w.n_seg = (d.V + be - 1) / be;
+  const int we = topk_wave_elems(d.logit_dtype);
+  w.n_sub = (d.V + we - 1) / we;
+  w.spb = topk_spb(R, w.n_sub);
+  w.n_seg = (w.n_sub + w.spb - 1) / w.spb;
   w.n_chunk = (d.V + kChunk - 1) / kChunk;
   size_t o = 0;
-  w.topk_partial = o; o = align256(o + (w.n_seg > 1 ? R * w.n_seg * 16 * sizeof(uint64_t) : 0));
-  w.topk_counter = o; o = align256(o + R * sizeof(uint32_t));
+  w.topk_partial = o; o = align256(o + R * w.n_seg * 16 * sizeof(uint64_t));
   w.gate = o;         o = align256(o + R * d.r * sizeof(float));
   w.cand_idx = o;     o = align256(o + R * d.K * sizeof(int32_t));
   w.cand_logit = o;   o = align256(o + R * d.K * sizeof(float));
+  w.zc = o;           o = align256(o + R * d.K * sizeof(float));
   w.S = o;            o = align256(o + R * d.K * d.K * sizeof(float));
   w.path_rank = o;    o = align256(o + R * sizeof(int32_t));
   w.draft_tok = o;    o = align256(o + R * sizeof(int32_t));
@@ -259,7 +277,7 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
     hipStream_t st = (hipStream_t)stream;
     dfk::ChunkStat* stats = reinterpret_cast<dfk::ChunkStat*>(static_cast<char*>(ws) + w.stats);
     if (dflash_status s = hip_status(timed(DFLASH_KERNEL_STATS, st, [&] {
-          return dfk::launch_stats(*d, w, Z, cand_idx, T, stats, st);
+          return dfk::launch_stats(*d, w, Z, T, stats, st);
         }), "stats launch")) return s;
     return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
       return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
@@ -289,24 +307,16 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, c
     int32_t* path_rank = path_rank_opt ? path_rank_opt : reinterpret_cast<int32_t*>(base + w.path_rank);
     int32_t* draft_tok = draft_tok_opt ? draft_tok_opt : reinterpret_cast<int32_t*>(base + w.draft_tok);
     float* q = q_opt ? q_opt : reinterpret_cast<float*>(base + w.q);
-    float* g = reinterpret_cast<float*>(base + w.gate);
-    dfk::ChunkStat* stats = reinterpret_cast<dfk::ChunkStat*>(base + w.stats);
     hipStream_t st = (hipStream_t)stream;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TOPK, st, [&] {
-          return dfk::launch_topk(*d, w, U, cand_idx, cand_logit, base, st);
-        }), "topk launch")) return s;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_GATE, st, [&] { return dfk::launch_gate(*d, h, W_g, g, st); }), "gate launch")) return s;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_SCORES, st, [&] {
-          return dfk::launch_scores(*d, x0, cand_idx, cand_logit, E, g, S, st);
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_STREAM, st, [&] {
+          return dfk::launch_cycle_stream(*d, w, U, Z, h, W_g, T, base, st);
+        }), "stream launch")) return s;
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
+          return dfk::launch_cycle_scores(*d, w, x0, E, Z, base, cand_idx, cand_logit, S, st);
         }), "scores launch")) return s;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TRACE, st, [&] {
-          return dfk::launch_trace(*d, S, cand_idx, T, seed, cycle, path_rank, draft_tok, q, st);
-        }), "trace launch")) return s;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_STATS, st, [&] {
-          return dfk::launch_stats(*d, w, Z, cand_idx, T, stats, st);
-        }), "stats launch")) return s;
-    return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
-      return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
+    return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
+      return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, S, T, seed, cycle, base, path_rank, draft_tok, q,
+                                        accept_len, out_tok, st);
     }), "finalize launch");
   } catch (...) {
     return fail(DFLASH_ERR_HIP, "internal error");
@@ -336,7 +346,8 @@ dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* 
 }
 
 const char* dflash_kernel_name(int32_t kernel) {
-  static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize"};
+  static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize",
+                                                   "cycle_stream", "cycle_scores", "cycle_finalize"};
   return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
 }
 

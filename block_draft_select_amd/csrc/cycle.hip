@@ -1,0 +1,182 @@
+// dflash_cycle: the whole draft -> select -> verify cycle in three launches
+// on the caller's stream.
+//   1. stream_kernel: one grid streams every logit once.  Its first blocks
+//      compute the gate tiles (they depend only on h and W_g), the next ones
+//      fold the drafter rows into sorted top lists (S1), the last ones reduce
+//      the target rows to chunk statistics (S5).  Nothing in the launch waits
+//      on anything else in it.
+//   2. cand_scores_kernel: one block per edge (b, t) merges the top lists of
+//      rows t-1 and t, writes row t's candidates (and their target logits),
+//      and computes the edge's pair scores (S2, S3).
+//   3. trace_finalize_kernel: one block per stream walks the trace (S4, one
+//      wave) while the other waves combine the chunk statistics, then runs
+//      the accept tests and the residual/bonus draw (S6).
+#include "stats_blocks.hpp"
+#include "topk_blocks.hpp"
+
+namespace dfk {
+
+namespace {
+
+union StreamLds {
+  struct {
+    TkWave sw[4];
+    uint64_t block_top[16];
+  } tk;
+  float red[kGateRed];
+};
+
+template <int DT, int PT>
+__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U, const void* __restrict__ Z,
+                                                     const void* __restrict__ h, const void* __restrict__ W, int R,
+                                                     int H, int r, float* __restrict__ g, int n_gate, int gate_cols,
+                                                     int V, int K, int L, int n_sub, int spb, int n_seg,
+                                                     uint64_t* __restrict__ partial, int n_chunk, int n_grp,
+                                                     const float* __restrict__ T, ChunkStat* __restrict__ stats) {
+  __shared__ StreamLds sh;
+  int id = blockIdx.x;
+  if (id < n_gate) {
+    if (PT == DFLASH_BF16)
+      gate_tile_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, g,
+                     id / gate_cols, id - (id / gate_cols) * gate_cols, sh.red);
+    else
+      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, g, id);
+    return;
+  }
+  id -= n_gate;
+  const int n_topk = R * n_seg;
+  if (id < n_topk) {
+    const int row = id / n_seg, seg = id - row * n_seg;
+    topk_block<DT>(U, V, K, n_sub, spb, row, seg, sh.tk.sw, sh.tk.block_top,
+                   partial + ((size_t)row * n_seg + seg) * 16);
+    return;
+  }
+  id -= n_topk;
+  const int rowid = id / n_grp;
+  const int c = (id - rowid * n_grp) * 4 + (threadIdx.x >> 6);
+  if (c >= n_chunk) return;
+  const int lane = threadIdx.x & 63;
+  const ChunkStat st = stats_chunk<DT>(Z, (size_t)rowid, V, c, T[rowid / (L + 1)], lane);
+  if (lane == 0) stats[(size_t)rowid * n_chunk + c] = st;
+}
+
+struct CandLds {
+  EdgeLds e;
+  uint64_t keys[2 * kTopkCycleMerge];
+  uint64_t prev[16], cur[16];
+};
+
+template <int DT, int PT>
+__global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __restrict__ partial, int n_seg,
+                                                          const int32_t* __restrict__ x0, const void* __restrict__ E,
+                                                          const float* __restrict__ g, const void* __restrict__ Z,
+                                                          int L, int V, int K, int r, int32_t* __restrict__ cand_idx,
+                                                          float* __restrict__ cand_logit, float* __restrict__ zc,
+                                                          float* __restrict__ S) {
+  __shared__ CandLds cl;
+  const int bt = blockIdx.x;
+  const int b = bt / L, t = bt - b * L;
+  const int tid = threadIdx.x;
+  if (tid < 16) cl.prev[tid] = cl.cur[tid] = 0ull;
+  merge_two_rows(partial + (size_t)(t > 0 ? bt - 1 : bt) * n_seg * 16, t > 0, partial + (size_t)bt * n_seg * 16,
+                 n_seg, K, cl.keys, cl.prev, cl.cur);
+  if (tid < 16) {
+    int p = -1, c = -1;
+    float v = 0.f;
+    if (tid < K) {
+      p = t == 0 ? clamp_idx(x0[b], V) : key_index(cl.prev[tid]);
+      c = key_index(cl.cur[tid]);
+      v = key_value(cl.cur[tid]);
+      const size_t o = (size_t)bt * K + tid;
+      cand_idx[o] = c;
+      cand_logit[o] = v;
+      const size_t zi = ((size_t)b * (L + 1) + t) * V + c;
+      zc[o] = DT == DFLASH_BF16
+                  ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
+                  : reinterpret_cast<const float*>(Z)[zi];
+    } else if (t == 0) {
+      p = clamp_idx(x0[b], V);
+    }
+    cl.e.pidx[tid] = p;
+    cl.e.cidx[tid] = c;
+    cl.e.cl[tid] = v;
+  }
+  __syncthreads();
+  edge_scores<PT>(cl.e, E, g + (size_t)bt * r, K, r, S + (size_t)bt * K * K);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
+    const void* __restrict__ Z, int L, int V, int K, int n_chunk, const float* __restrict__ T,
+    const uint64_t* __restrict__ seed, uint64_t cycle, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ zc, const float* __restrict__ S, int32_t* __restrict__ path_rank,
+    int32_t* __restrict__ draft_tok, float* __restrict__ q, const ChunkStat* __restrict__ stats,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
+  __shared__ FinLds f;
+  finalize_stream<DT, true>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank,
+                            draft_tok, q, stats, accept_len, out_tok);
+}
+
+}  // namespace
+
+hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
+                               const void* W_g, const float* T, char* ws, hipStream_t st) {
+  const int R = d.B * d.L;
+  const int gate_cols = (d.r + 63) / 64;
+  const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols : R;
+  const int n_grp = (w.n_chunk + 3) / 4;
+  const long long blocks = (long long)n_gate + (long long)R * w.n_seg + (long long)d.B * (d.L + 1) * n_grp;
+  float* g = reinterpret_cast<float*>(ws + w.gate);
+  uint64_t* partial = reinterpret_cast<uint64_t*>(ws + w.topk_partial);
+  ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws + w.stats);
+#define DF_STREAM(DT, PT)                                                                                     \
+  hipLaunchKernelGGL((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), 0, st, U, Z, h, W_g, R,      \
+                     d.hidden, d.r, g, n_gate, gate_cols, d.V, d.K, d.L, w.n_sub, w.spb, w.n_seg, partial,     \
+                     w.n_chunk, n_grp, T, stats)
+  if (d.logit_dtype == DFLASH_BF16) {
+    if (d.param_dtype == DFLASH_BF16) DF_STREAM(DFLASH_BF16, DFLASH_BF16); else DF_STREAM(DFLASH_BF16, DFLASH_F32);
+  } else {
+    if (d.param_dtype == DFLASH_BF16) DF_STREAM(DFLASH_F32, DFLASH_BF16); else DF_STREAM(DFLASH_F32, DFLASH_F32);
+  }
+#undef DF_STREAM
+  return hipGetLastError();
+}
+
+hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,
+                               const void* Z, char* ws, int32_t* cand_idx, float* cand_logit, float* S,
+                               hipStream_t st) {
+  const dim3 grid((unsigned)(d.B * d.L));
+  const uint64_t* partial = reinterpret_cast<const uint64_t*>(ws + w.topk_partial);
+  const float* g = reinterpret_cast<const float*>(ws + w.gate);
+  float* zc = reinterpret_cast<float*>(ws + w.zc);
+#define DF_SCORES(DT, PT)                                                                                      \
+  hipLaunchKernelGGL((cand_scores_kernel<DT, PT>), grid, dim3(256), 0, st, partial, w.n_seg, x0, E, g, Z, d.L, \
+                     d.V, d.K, d.r, cand_idx, cand_logit, zc, S)
+  if (d.logit_dtype == DFLASH_BF16) {
+    if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);
+  } else {
+    if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_F32, DFLASH_BF16); else DF_SCORES(DFLASH_F32, DFLASH_F32);
+  }
+#undef DF_SCORES
+  return hipGetLastError();
+}
+
+hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
+                                 const float* S, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
+                                 int32_t* out_tok, hipStream_t st) {
+  const dim3 grid((unsigned)d.B);
+  const float* zc = reinterpret_cast<const float*>(ws + w.zc);
+  const ChunkStat* stats = reinterpret_cast<const ChunkStat*>(ws + w.stats);
+  if (d.logit_dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(trace_finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K,
+                       w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
+                       out_tok);
+  else
+    hipLaunchKernelGGL(trace_finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K,
+                       w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
+                       out_tok);
+  return hipGetLastError();
+}
+
+}  // namespace dfk

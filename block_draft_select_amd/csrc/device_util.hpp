@@ -62,6 +62,89 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// ---------------------------------------------------------------- DPP scans
+// Cross-lane steps through the data-parallel-primitive (DPP) modifiers of
+// GFX9: a lane reads another lane's register in the same instruction, with
+// no LDS round trip.  Lanes whose source is outside their row, or whose row
+// is masked off, receive `id` (the identity of the operation).
+
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v, float id) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v), __float_as_uint(id)));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v, double id) {
+  const uint64_t b = __double_as_longlong(v), i = __double_as_longlong(id);
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)b, (uint32_t)i);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(b >> 32), (uint32_t)(i >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// inclusive prefix sum over lanes 0..15 of each row (fp64)
+__device__ __forceinline__ double row16_scan_f64(double v) {
+  v += dpp_f64<kDppRowShr1>(v, 0.0);
+  v += dpp_f64<kDppRowShr2>(v, 0.0);
+  v += dpp_f64<kDppRowShr4>(v, 0.0);
+  v += dpp_f64<kDppRowShr8>(v, 0.0);
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes (fp64)
+__device__ __forceinline__ double wave_scan_f64(double v) {
+  v = row16_scan_f64(v);
+  v += dpp_f64<kDppRowBcast15, 0xA>(v, 0.0);
+  v += dpp_f64<kDppRowBcast31, 0xC>(v, 0.0);
+  return v;
+}
+
+// running maximum over lanes 0..15 of each row (fp32); lane 15 holds the row max
+__device__ __forceinline__ float row16_scan_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kDppRowShr1>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kDppRowShr2>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kDppRowShr4>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kDppRowShr8>(v, -INFINITY));
+  return v;
+}
+
+// maximum over the 64 lanes (fp32), the same value in every lane
+__device__ __forceinline__ float wave_max_dpp_f32(float v) {
+  v = row16_scan_max_f32(v);
+  v = fmaxf(v, dpp_f32<kDppRowBcast15, 0xA>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kDppRowBcast31, 0xC>(v, -INFINITY));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+// sum over the 64 lanes (fp64), the same value in every lane
+__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
+  v = wave_scan_f64(v);
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// lowest lane whose predicate holds (64 if none)
+__device__ __forceinline__ int first_lane(bool pred) {
+  const uint64_t m = __ballot(pred);
+  return m ? __builtin_ctzll(m) : 64;
+}
+
 // ------------------------------------------------------- ordered keys
 // An order-preserving map from IEEE bit patterns to unsigned integers:
 // non-negative values get the sign bit set, negative values are inverted.

@@ -19,6 +19,10 @@ constexpr int kTopkMergeMax = 2048;    // keys the last block of a row merges in
 
 inline int topk_wave_elems(int logit_dtype) { return 64 * kTopkLoads * (logit_dtype == DFLASH_BF16 ? 8 : 4); }
 inline int topk_block_elems(int logit_dtype) { return 4 * topk_wave_elems(logit_dtype); }
+// blocks per drafter row stay <= 32 so that the partial lists of two rows
+// fit the cycle's candidate/score block (kTopkCycleMerge keys of LDS)
+constexpr int kTopkCycleMerge = 512;
+constexpr int kTopkMaxSeg = kTopkCycleMerge / 16;
 
 constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
 
@@ -30,9 +34,11 @@ struct ChunkStat {
 };
 
 struct WsLayout {
-  int n_seg;    // top-K segments per drafter row
+  int n_sub;    // top-K sub-segments (one wave's registers) per drafter row
+  int spb;      // sub-segments per top-K block
+  int n_seg;    // top-K blocks per drafter row (a merge kernel runs if > 1)
   int n_chunk;  // target chunks per row
-  size_t topk_partial, topk_counter, gate, cand_idx, cand_logit, S, path_rank, draft_tok, q, stats;
+  size_t topk_partial, gate, cand_idx, cand_logit, zc, S, path_rank, draft_tok, q, stats;
   size_t total;
 };
 
@@ -49,13 +55,24 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
                         const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
                         float* q, hipStream_t st);
-hipError_t launch_stats(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
-                        const float* T, ChunkStat* stats, hipStream_t st);
+hipError_t launch_stats(const dflash_dims& d, const WsLayout& w, const void* Z, const float* T, ChunkStat* stats,
+                        hipStream_t st);
 hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* Z,
                            const int32_t* cand_idx, const int32_t* path_rank, const float* q,
                            const float* T, const uint64_t* seed, uint64_t cycle,
                            const ChunkStat* stats, int32_t* accept_len, int32_t* out_tok,
                            hipStream_t st);
+// dflash_cycle: (1) gate + top-K lists + chunk statistics, (2) candidates
+// + pair scores, (3) trace + verify
+hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
+                               const void* W_g, const float* T, char* ws, hipStream_t st);
+hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,
+                               const void* Z, char* ws, int32_t* cand_idx, float* cand_logit, float* S,
+                               hipStream_t st);
+hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
+                                 const float* S, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
+                                 int32_t* out_tok, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st);

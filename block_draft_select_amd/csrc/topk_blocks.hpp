@@ -1,0 +1,391 @@
+// Device building blocks of S1 (top-K candidates of every drafter row; P1
+// "DFlash 2: Block diffusion, wearing a drafter's coat", section "Sixteen
+// candidates per position").
+//
+// Drafter rows are streamed once from HBM with 16-byte loads.  A row is cut
+// into sub-segments of 64 x 64 values (bf16; 64 x 32 fp32): one wave holds a
+// whole sub-segment in registers and folds it into its running top list in
+// two passes over those registers:
+//   1. one value per lane (a packed signed 16-bit max of the raw bf16
+//      patterns picks the lane maximum whenever the lane holds a
+//      non-negative value, and some value of the lane otherwise), then the
+//      K-th largest pick by a 16-step ballot bisection: at least K values
+//      of the sub-segment are at or above it.  The running list's K-th key
+//      (plus one: later indices lose ties) is a second lower bound; the
+//      larger one is the threshold;
+//   2. values at or above the threshold are appended to an LDS buffer next
+//      to the running list and merged into it by exact rank (value desc,
+//      index asc).
+// A tie-heavy sub-segment whose candidates overflow the buffer takes an
+// out-of-line exact path that re-reads it.  A block (4 waves) owns a run of
+// sub-segments and writes the sorted top list of that run; the lists of a
+// row are merged by binary-search ranking.  Results do not depend on the
+// segmentation because the order is total.
+#pragma once
+
+#include "device_util.hpp"
+#include "internal.hpp"
+
+namespace dfk {
+
+struct TkWave {
+  uint64_t buf[kTopkCap];
+  uint64_t top[16];  // running list, sorted, zero = empty
+  uint32_t cnt;
+  uint32_t ntop;
+};
+
+// 64-bit candidate key: ordered value in the high word, inverted index low
+__device__ __forceinline__ uint64_t make_key(uint32_t ord_value, uint32_t idx) {
+  return ((uint64_t)ord_value << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+// number of entries of a descending list (zeros last) greater than key
+__device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64_t key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > key) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Merge the buffered keys into the running list.  buf[0, ntop) is the
+// running list (sorted, descending); buf[ntop, cnt) holds new candidates in
+// any order; all keys are distinct and non-zero.  A running key's new rank
+// is its position plus the number of larger new keys; a new key's rank is
+// the number of larger running keys (binary search) plus larger new keys.
+__device__ void merge_buffer(TkWave& w, int K, int lane) {
+  const uint32_t ntop = w.ntop;
+  const uint32_t c = min(w.cnt, (uint32_t)kTopkCap);
+  if (c == ntop) return;  // nothing new
+  uint64_t mine[(kTopkCap + 16) / kWave + 1];
+  uint32_t rank[(kTopkCap + 16) / kWave + 1];
+  constexpr int SL = (kTopkCap + 16) / kWave + 1;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const uint32_t i = lane + s * kWave;
+    mine[s] = i < c ? w.buf[i] : 0ull;
+    rank[s] = i < ntop ? i : (i < c ? (uint32_t)count_greater(w.buf, (int)ntop, mine[s]) : 0xFFFFu);
+  }
+  for (uint32_t j = ntop; j < c; ++j) {
+    const uint64_t o = w.buf[j];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) rank[s] += (o > mine[s]) ? 1u : 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int s = 0; s < SL; ++s)
+    if (mine[s] != 0ull && rank[s] < (uint32_t)K) w.top[rank[s]] = mine[s];
+  if (lane == 0) w.ntop = min(c, (uint32_t)K);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
+// bf16 element of sub-segment [lo, hi) held by `lane` in slot s (0..63):
+// load j = s / 8, position e = s % 8, index lo + (j * 64 + lane) * 8 + e
+__device__ __forceinline__ int slot_index_bf16(int lo, int lane, int s) {
+  return lo + ((s >> 3) * kWave + lane) * 8 + (s & 7);
+}
+
+// Exact top-K of one sub-segment whose threshold admits too many values
+// (long runs of equal values).  Re-reads the sub-segment on every bisection
+// step, so the hot path keeps no extra registers; appends K keys to the
+// buffer after its first `base` entries.
+template <int DT>
+__device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int hi, int K, int lane,
+                                              TkWave& w, uint32_t base) {
+  constexpr int NS = DT == DFLASH_BF16 ? 64 : 32;
+  constexpr int VBITS = DT == DFLASH_BF16 ? 16 : 32;
+  // canonical value key (-0 folded onto +0) of slot s, 0 outside [lo, hi)
+  auto cv = [&](int s, int& idx) -> uint32_t {
+    if (DT == DFLASH_BF16) {
+      idx = slot_index_bf16(lo, lane, s);
+      if (idx >= hi) return 0u;
+      const uint32_t b = reinterpret_cast<const uint16_t*>(row_ptr)[idx];
+      const uint32_t k = ord16x2(b) & 0xFFFFu;
+      return k == 0x7FFFu ? 0x8000u : k;
+    } else {
+      idx = lo + ((s >> 2) * kWave + lane) * 4 + (s & 3);
+      if (idx >= hi) return 0u;
+      return ord32_canon(reinterpret_cast<const uint32_t*>(row_ptr)[idx]);
+    }
+  };
+  uint32_t tv = 0;
+  for (int bit = VBITS - 1; bit >= 0; --bit) {
+    const uint32_t c = tv | (1u << bit);
+    uint32_t n = 0;
+    for (int s = 0; s < NS; ++s) {
+      int idx;
+      n += (cv(s, idx) >= c) ? 1u : 0u;
+    }
+    if (wave_sum_u32(n) >= (uint32_t)K) tv = c;
+  }
+  uint32_t gt = 0;
+  for (int s = 0; s < NS; ++s) {
+    int idx;
+    gt += (cv(s, idx) > tv) ? 1u : 0u;
+  }
+  gt = wave_sum_u32(gt);
+  const uint32_t need = (uint32_t)K > gt ? (uint32_t)K - gt : 0u;
+  // smallest index x with #(value == tv, index <= x) >= need
+  int xlo = lo, xhi = hi - 1;
+  while (xlo < xhi) {
+    const int mid = (xlo + xhi) >> 1;
+    uint32_t n = 0;
+    for (int s = 0; s < NS; ++s) {
+      int idx;
+      n += (cv(s, idx) == tv && idx <= mid) ? 1u : 0u;
+    }
+    if (wave_sum_u32(n) >= need) xhi = mid; else xlo = mid + 1;
+  }
+  if (lane == 0) w.cnt = base;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int s = 0; s < NS; ++s) {
+    int idx;
+    const uint32_t v = cv(s, idx);
+    if (v != 0u && (v > tv || (v == tv && need > 0 && idx <= xlo))) {
+      const uint32_t ord = DT == DFLASH_BF16 ? ord32_of_k16(v) : v;
+      const uint32_t pos = atomicAdd(&w.cnt, 1u);
+      if (pos < (uint32_t)kTopkCap) w.buf[pos] = make_key(ord, (uint32_t)idx);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t max_i16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, a),
+                                                                __builtin_bit_cast(s16x2, b)));
+}
+
+// append the candidates of one register (two bf16 patterns) whose 16-bit
+// ordered key is >= thr
+__device__ __forceinline__ void collect_pair(uint32_t raw, int idx0, uint32_t thr, TkWave& w) {
+  const uint32_t k2 = ord16x2(raw);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t k16 = h ? (k2 >> 16) : (k2 & 0xFFFFu);
+    if (k16 >= thr) {
+      const uint32_t pos = atomicAdd(&w.cnt, 1u);
+      if (pos < (uint32_t)kTopkCap) w.buf[pos] = make_key(ord32_of_k16(k16), (uint32_t)(idx0 + h));
+    }
+  }
+}
+
+// Fold bf16 sub-segment [lo, hi) of `row` into the wave's running list.
+// Registers keep the raw patterns.  A packed signed 16-bit max picks one
+// actual value per lane (the lane maximum whenever the lane holds a
+// non-negative value); the K-th largest of those picks is a valid
+// threshold.  When the threshold is positive, a raw pattern passes exactly
+// when it is >= the threshold's pattern as a signed 16-bit integer, so the
+// candidate test needs no key transform.
+__device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
+  constexpr int WS = 64 * kTopkLoads * 8;
+  uint32_t x[4 * kTopkLoads];
+  if (hi - lo == WS) {
+#pragma unroll
+    for (int j = 0; j < kTopkLoads; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 8);
+      x[4 * j + 0] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTopkLoads; ++j) {
+      const int base = lo + (j * kWave + lane) * 8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t e0 = (base + 2 * c < hi) ? (uint32_t)row[base + 2 * c] : 0xFFFFu;
+        const uint32_t e1 = (base + 2 * c + 1 < hi) ? (uint32_t)row[base + 2 * c + 1] : 0xFFFFu;
+        x[4 * j + c] = e0 | (e1 << 16);  // 0xFFFF: key 0, never admitted
+      }
+    }
+  }
+  uint32_t m = x[0];
+#pragma unroll
+  for (int q = 1; q < 4 * kTopkLoads; ++q) m = max_i16x2(m, x[q]);
+  const int pick = max((int)(int16_t)(m & 0xFFFFu), (int)(int16_t)(m >> 16));
+  const uint32_t pick_key = ord16x2((uint32_t)pick & 0xFFFFu) & 0xFFFFu;
+
+  // K-th largest pick
+  uint32_t thr = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    if (__popcll(__ballot(pick_key >= c)) >= (unsigned)K) thr = c;
+  }
+  if (thr == 0x8000u) thr = 0x7FFFu;  // a +0.0 threshold also admits -0.0
+  if (thr == 0u) thr = 1u;            // never admit padding
+  const uint32_t ntop = w.ntop;
+  if (ntop == (uint32_t)K) thr = max(thr, (uint32_t)(w.top[K - 1] >> 48) + 1u);
+
+  // buffer = running list, then the new candidates
+  if (lane < (int)ntop) w.buf[lane] = w.top[lane];
+  if (lane == 0) w.cnt = ntop;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (thr > 0x8000u && thr <= 0xFFFFu) {
+    const uint32_t tm1 = ((thr & 0x7FFFu) - 1u) * 0x00010001u;  // positive pattern - 1, both halves
+#pragma unroll
+    for (int q = 0; q < 4 * kTopkLoads; ++q)
+      if (max_i16x2(x[q], tm1) != tm1)
+        collect_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w);
+  } else if (thr <= 0xFFFFu) {
+    const uint32_t tm1 = (thr - 1u) * 0x00010001u;
+#pragma unroll
+    for (int q = 0; q < 4 * kTopkLoads; ++q)
+      if (subsat_u16x2(ord16x2(x[q]), tm1) != 0u)
+        collect_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (w.cnt > (uint32_t)kTopkCap) exact_subsegment<DFLASH_BF16>(row, lo, hi, K, lane, w, ntop);
+  merge_buffer(w, K, lane);
+}
+
+// fold fp32 sub-segment [lo, hi) of `row` into the wave's running list
+__device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
+  constexpr int WS = 64 * kTopkLoads * 4;
+  uint32_t kx[4 * kTopkLoads];
+  if (hi - lo == WS) {
+#pragma unroll
+    for (int j = 0; j < kTopkLoads; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 4);
+      kx[4 * j + 0] = ord32(v.x);
+      kx[4 * j + 1] = ord32(v.y);
+      kx[4 * j + 2] = ord32(v.z);
+      kx[4 * j + 3] = ord32(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTopkLoads; ++j) {
+      const int base = lo + (j * kWave + lane) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kx[4 * j + c] = (base + c < hi) ? ord32(row[base + c]) : 0u;
+    }
+  }
+  uint32_t lanemax = kx[0];
+#pragma unroll
+  for (int q = 1; q < 4 * kTopkLoads; ++q) lanemax = max(lanemax, kx[q]);
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    if (__popcll(__ballot(lanemax >= c)) >= (unsigned)K) thr = c;
+  }
+  if (thr == 0x80000000u) thr = 0x7FFFFFFFu;
+  if (thr == 0u) thr = 1u;
+  const uint32_t ntop = w.ntop;
+  bool none = false;
+  if (ntop == (uint32_t)K) {
+    const uint32_t t = (uint32_t)(w.top[K - 1] >> 32);
+    if (t == 0xFFFFFFFFu) none = true; else thr = max(thr, t + 1u);
+  }
+  if (lane < (int)ntop) w.buf[lane] = w.top[lane];
+  if (lane == 0) w.cnt = ntop;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (!none) {
+#pragma unroll
+    for (int q = 0; q < 4 * kTopkLoads; ++q) {
+      if (kx[q] >= thr) {
+        const uint32_t canon = kx[q] == 0x7FFFFFFFu ? 0x80000000u : kx[q];
+        const int idx = lo + ((q >> 2) * kWave + lane) * 4 + (q & 3);
+        const uint32_t pos = atomicAdd(&w.cnt, 1u);
+        if (pos < (uint32_t)kTopkCap) w.buf[pos] = make_key(canon, (uint32_t)idx);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (w.cnt > (uint32_t)kTopkCap) exact_subsegment<DFLASH_F32>(row, lo, hi, K, lane, w, ntop);
+  merge_buffer(w, K, lane);
+}
+
+
+// The sorted top list (16 keys, zero-padded) of sub-segments
+// [seg * spb, min((seg + 1) * spb, n_sub)) of drafter row `row`, computed by
+// a 256-thread block and written to `out16` (global).  `sw` is LDS for 4
+// waves, `block_top` 16 LDS keys.
+template <int DT>
+__device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, int K, int n_sub, int spb, int row,
+                                           int seg, TkWave* sw, uint64_t* block_top, uint64_t* __restrict__ out16) {
+  constexpr int WS = 64 * kTopkLoads * (DT == DFLASH_BF16 ? 8 : 4);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  TkWave& w = sw[wave];
+  if (lane < 16) w.top[lane] = 0ull;
+  if (lane == 0) w.ntop = 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int s1 = min((seg + 1) * spb, n_sub);
+  for (int s = seg * spb + wave; s < s1; s += 4) {
+    const int lo = s * WS, hi = min(lo + WS, V);
+    if (DT == DFLASH_BF16)
+      wave_fold_bf16(reinterpret_cast<const uint16_t*>(U) + (size_t)row * V, lo, hi, K, w, lane);
+    else
+      wave_fold_f32(reinterpret_cast<const uint32_t*>(U) + (size_t)row * V, lo, hi, K, w, lane);
+  }
+  if (tid < 16) block_top[tid] = 0ull;
+  __syncthreads();
+  // merge the four sorted wave lists: one key per thread of the first 64
+  if (tid < 64) {
+    const int lw = tid >> 4, k = tid & 15;
+    const uint64_t key = sw[lw].top[k];
+    if (key != 0ull && k < K) {
+      int rank = k;
+#pragma unroll
+      for (int o = 0; o < 4; ++o)
+        if (o != lw) rank += count_greater(sw[o].top, K, key);
+      if (rank < K) block_top[rank] = key;
+    }
+  }
+  __syncthreads();
+  if (tid < 16) out16[tid] = block_top[tid];
+}
+
+// Merge the n_seg sorted lists of one row (global, 16 keys each) into the
+// row's sorted top-K keys `out` (LDS, K entries), using `keys` (LDS, at
+// least n_seg * 16 entries) as staging.  Every thread of the block takes
+// part; ends with a barrier.
+__device__ __forceinline__ void merge_row(const uint64_t* __restrict__ lists, int n_seg, int K, uint64_t* keys,
+                                          uint64_t* out) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int nk = n_seg * 16;
+  for (int i = tid; i < nk; i += nt) keys[i] = lists[i];
+  __syncthreads();
+  for (int i = tid; i < nk; i += nt) {
+    const int s = i >> 4, k = i & 15;
+    const uint64_t key = keys[i];
+    if (key == 0ull || k >= K) continue;
+    int rank = k;
+    for (int s2 = 0; s2 < n_seg && rank < K; ++s2)
+      if (s2 != s) rank += count_greater(keys + s2 * 16, K, key);
+    if (rank < K) out[rank] = key;
+  }
+  __syncthreads();
+}
+
+// Merge the lists of rows r0 and r1 (global; r0 may be absent: n0 = 0) into
+// out0 / out1 (LDS, K entries each) in one pass; `keys` holds at least
+// 2 * n_seg * 16 entries.  Every thread of the block takes part; ends with
+// a barrier.
+__device__ __forceinline__ void merge_two_rows(const uint64_t* __restrict__ lists0, bool has0,
+                                               const uint64_t* __restrict__ lists1, int n_seg, int K, uint64_t* keys,
+                                               uint64_t* out0, uint64_t* out1) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int nk = n_seg * 16;
+  for (int i = tid; i < 2 * nk; i += nt)
+    keys[i] = i < nk ? (has0 ? lists0[i] : 0ull) : lists1[i - nk];
+  __syncthreads();
+  for (int i = tid; i < 2 * nk; i += nt) {
+    const int half = i >= nk, j = i - half * nk;
+    const int s = j >> 4, k = j & 15;
+    const uint64_t key = keys[i];
+    if (key == 0ull || k >= K) continue;
+    const uint64_t* base = keys + half * nk;
+    int rank = k;
+    for (int s2 = 0; s2 < n_seg && rank < K; ++s2)
+      if (s2 != s) rank += count_greater(base + s2 * 16, K, key);
+    if (rank < K) (half ? out1 : out0)[rank] = key;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ float key_value(uint64_t key) { return __uint_as_float(unord32((uint32_t)(key >> 32))); }
+
+}  // namespace dfk

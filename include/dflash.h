@@ -78,7 +78,7 @@ enum {
 enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 };
 
 typedef struct dflash_dims {
-  int32_t B;           /* streams, >= 1 */
+  int32_t B;           /* streams, >= 1, B * (L + 1) <= 65535 */
   int32_t L;           /* drafted positions, 1..DFLASH_L_MAX */
   int32_t V;           /* vocabulary, K..DFLASH_V_MAX; V * sizeof(logit) % 16 == 0 */
   int32_t K;           /* candidates per position, 1..DFLASH_K_MAX */
@@ -114,14 +114,16 @@ dflash_status dflash_topk(const dflash_dims* d, const void* U, int32_t* cand_idx
                           float* cand_logit, void* ws, size_t ws_bytes, void* stream);
 
 /* S2 + S3 -- context gate and adjacent pair scores (P3 "A Lightweight Path
- * Selector"; P1 "A path selector").  With g_t = sigmoid(h_t @ W_g):
+ * Selector"; P1 "A path selector").  With g_t[k] = sigmoid(sum_j
+ * W_g[k,j] * h_t[j]):
  *   S[b,t,i,j] = cand_logit[b,t,j] + sum_k E[a_i,k] * g_t[k] * E[c_j,k]
  * where c_j = cand_idx[b,t,j] and a_i = cand_idx[b,t-1,i] for t >= 1, and
  * a_i = x0[b] (the last verified token) for every row i of edge t = 0.
  *   x0         [B] int32, the last verified token of each stream
  *   cand_idx   [B, L, K] int32, cand_logit [B, L, K] float (from dflash_topk)
  *   E          [V, r] candidate embeddings (param_dtype)
- *   W_g        [hidden, r] gate weights (param_dtype)
+ *   W_g        [r, hidden] gate weights (param_dtype), one row per
+ *              embedding dimension (the layout of a linear layer's weight)
  *   h          [B, L, hidden] drafter context (param_dtype)
  *   S          [B, L, K, K] float out (rows: predecessor rank, cols: rank) */
 dflash_status dflash_pair_scores(const dflash_dims* d, const int32_t* x0,
@@ -167,7 +169,7 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
                             int32_t* out_tok, void* ws, size_t ws_bytes, void* stream);
 
 /* One whole cycle: dflash_topk, dflash_pair_scores, dflash_trace and
- * dflash_verify on one stream, with identical results.  The intermediate
+ * dflash_verify on one stream, with identical results, in three launches.  The intermediate
  * outputs (cand_idx [B,L,K], cand_logit [B,L,K], S [B,L,K,K],
  * path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written where the
  * caller passes non-NULL pointers and kept in the workspace otherwise. */
@@ -197,7 +199,10 @@ enum {
   DFLASH_KERNEL_TRACE = 3,
   DFLASH_KERNEL_STATS = 4,
   DFLASH_KERNEL_FINALIZE = 5,
-  DFLASH_KERNEL_COUNT = 6
+  DFLASH_KERNEL_CYCLE_STREAM = 6,   /* dflash_cycle: gate + top-K lists + target chunk statistics */
+  DFLASH_KERNEL_CYCLE_SCORES = 7,   /* dflash_cycle: candidates + pair scores */
+  DFLASH_KERNEL_CYCLE_FINALIZE = 8, /* dflash_cycle: trace + verify */
+  DFLASH_KERNEL_COUNT = 9
 };
 
 /* Name of a kernel identifier ("" if out of range). */

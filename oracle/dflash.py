@@ -19,11 +19,12 @@ Notation.  One stream has a block of L drafted positions t = 1..L.  U_t is
 the drafter's logit row at position t (length V), h_t its context vector, x0
 the last verified token.  Z_t (t = 1..L+1) are the target's logit rows.
 C_t is the ordered list of K candidates at position t.  E is the [V, r]
-candidate-embedding table and W the [hidden, r] gate matrix.
+candidate-embedding table and W the [r, hidden] gate matrix (one row per
+embedding dimension, the layout of a linear layer's weight).
 
 Readings of points the pages leave open (each one is listed in the design doc):
   * score:   s_t(a, b) = U_t(b) + sum_k E[a,k] * g_t[k] * E[b,k],
-             g_t = sigmoid(h_t @ W)  (the formula itself was lost from P3);
+             g_t = sigmoid(W @ h_t)  (the formula itself was lost from P3);
   * edge 1 uses a = x0 for every row of its score matrix;
   * trace:   greedy left-to-right walk (T = 0) or a draw from
              softmax(s_t(a_{t-1}, .) / T) over C_t (T > 0); q_t is that
@@ -91,8 +92,11 @@ def topk_row(u_row, K):
 # --------------------------------------------------------------------------
 
 def gate(h_t, W):
-    """g_t = sigmoid(h_t @ W): one gate weight per embedding dimension."""
-    a = np.asarray(h_t, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+    """g_t = sigmoid(W @ h_t): one gate weight per embedding dimension.
+
+    ``W`` is [r, hidden]; row k holds the weights of gate dimension k.
+    """
+    a = np.asarray(W, dtype=np.float64) @ np.asarray(h_t, dtype=np.float64)
     return 1.0 / (1.0 + np.exp(-a))
 
 
@@ -313,7 +317,7 @@ def cycle_stream(inp, b, chunk=CHUNK):
     """All steps S1..S6 for stream ``b`` of an input set.
 
     ``inp`` is a mapping with keys B, L, V, K, r, hidden, logit_kind,
-    param_kind, U [B,L,V], Z [B,L+1,V], x0 [B], E [V,r], W [hidden,r],
+    param_kind, U [B,L,V], Z [B,L+1,V], x0 [B], E [V,r], W [r,hidden],
     h [B,L,hidden], T [B], seed [B], cycle (int).  Arrays hold storage
     values (uint16 bf16 patterns or float32); everything is widened here.
     """

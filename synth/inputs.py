@@ -15,7 +15,7 @@ of those is used.  These inputs only take their shapes and value structure:
 * target logits Z [B, L+1, V] = U + N(0, noise^2), rounded; row L+1 is a
   fresh drafter-like row plus noise;
 * x0 uniform over the vocabulary, E [V, r] ~ N(0, e_std^2),
-  W [hidden, r] ~ N(0, 0.02^2), h [B, L, hidden] ~ N(0, 1);
+  W [r, hidden] ~ N(0, 0.02^2), h [B, L, hidden] ~ N(0, 1);
 * T per stream; Philox seed of stream b = (config_id << 32) | b.
 
 All draws come from numpy.random.Generator(PCG64(SeedSequence([config_id,
@@ -163,7 +163,7 @@ def make(config_id, set_id=0, *, B=None, L=None, V=None, K=None, r=None,
         E = _store(np.zeros((Vn, rn), dtype=np.float32), pk)
     else:
         E = _store(rng.standard_normal((Vn, rn), dtype=np.float32) * np.float32(e_std), pk)
-    W = _store(rng.standard_normal((Hn, rn), dtype=np.float32) * np.float32(0.02), pk)
+    W = _store(rng.standard_normal((rn, Hn), dtype=np.float32) * np.float32(0.02), pk)
     h = _store(rng.standard_normal((Bn, Ln, Hn), dtype=np.float32), pk)
     x0 = rng.integers(0, Vn, size=Bn).astype(np.int32)
 

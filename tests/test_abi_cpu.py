@@ -69,11 +69,19 @@ def test_bad_dims_rejected(dfl, field, value, status):
     assert dfl.lib.dflash_cycle(ctypes.byref(d), *([None] * 8), 0, *([None] * 8), None, 0, None) == status
 
 
-def test_fp32_vocab_limit(dfl):
-    d = dfl.dims(1, 1, 1048576 + 4, 16, 16, 16, "f32", "f32")
-    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 2
-    d = dfl.dims(1, 1, 1048576, 16, 16, 16, "f32", "f32")
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_vocab_limit(dfl, kind):
+    d = dfl.dims(1, 1, dfl.V_MAX, 16, 16, 16, kind, kind)
     assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 0
+    d = dfl.dims(1, 1, dfl.V_MAX + 8, 16, 16, 16, kind, kind)
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 2
+
+
+def test_stream_row_limit(dfl):
+    d = dfl.dims(65535 // 9, 8, 4096, 16, 16, 16, "bf16", "bf16")
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 0
+    d = dfl.dims(65535 // 9 + 1, 8, 4096, 16, 16, 16, "bf16", "bf16")
+    assert dfl.lib.dflash_workspace_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == 2
 
 
 def test_null_and_misaligned_pointers_rejected(dfl):

@@ -21,16 +21,16 @@ from oracle import dflash
 # ---------------------------------------------------------------- gate
 
 def test_gate_zero_context_is_one_half():
-    W = np.random.default_rng(0).standard_normal((64, 32))
+    W = np.random.default_rng(0).standard_normal((32, 64))
     assert np.array_equal(dflash.gate(np.zeros(64), W), np.full(32, 0.5))
 
 
 def test_gate_single_input_closed_form():
-    # h = e_i selects row i of W: g = 1 / (1 + e^{-W[i]})
-    W = np.linspace(-4, 4, 5 * 8).reshape(5, 8)
+    # h = e_i selects column i of W: g = 1 / (1 + e^{-W[:, i]})
+    W = np.linspace(-4, 4, 8 * 5).reshape(8, 5)
     h = np.zeros(5)
     h[3] = 1.0
-    want = np.array([1.0 / (1.0 + math.exp(-w)) for w in W[3]])
+    want = np.array([1.0 / (1.0 + math.exp(-w)) for w in W[:, 3]])
     assert np.allclose(dflash.gate(h, W), want, rtol=0, atol=1e-15)
 
 
