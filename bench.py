@@ -6,7 +6,7 @@ scores, trace, target-row statistics and verify) for a whole batch of
 streams, with every input already resident in HBM.  Input sets rotate so
 that the timed working set exceeds twice the 256 MB last-level cache.
 
-Prints one JSON line (see README of the measurement in the design doc):
+Prints one JSON line:
   value      draft-verify cycles/s on one GPU
   roofline   achieved algorithmic GB/s of the dominant kernel vs 8 TB/s
   cpu_baseline  the float64 NumPy oracle on a bounded sample, host cores
@@ -83,16 +83,30 @@ def cpu_baseline(inp, seconds):
             "host_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
-def load_traffic(kernel):
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+def load_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary.
+
+    The summary (profiles/traffic_<kernel>_<workload>.txt, "key: value"
+    lines) holds FETCH_SIZE + WRITE_SIZE of the kernel scaled by what the
+    same counters read for a plain copy of known size.  It counts only
+    while the kernel sources are the ones it was taken on.
+    """
+    tag = workload.split(":", 1)[0].replace("-", "")
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{tag}.txt")
     if not os.path.exists(p):
         return None
+    kv = {}
     with open(p) as f:
-        t = json.load(f)
-    e = t.get(kernel)
-    if not e or e.get("source_sha") != kernel_source_sha():
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_source_sha():
         return None
-    return e.get("bytes_per_launch")
+    try:
+        return int(float(kv["bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -105,6 +119,10 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="plain copies of a logit-sized buffer first (calibrates hardware byte counters)")
+    ap.add_argument("--read-probe", type=int, default=3,
+                    help="passes of a plain streaming read over every input set's logits (read ceiling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -129,6 +147,16 @@ def main():
     d = dims_of(base)
     ws = dfl.workspace(d)
     out = alloc_outputs(base)
+
+    if args.copy_probe:
+        src = torch.ones(ub + zb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.copy_probe):
+            dfl.dflash_copy_probe(dst, src)
+        torch.cuda.synchronize()
+        _log(f"[bench] {args.copy_probe} copies of {ub + zb} bytes done")
+        del src, dst
 
     def step(i):
         dv = devs[i % n_sets]
@@ -164,13 +192,35 @@ def main():
     dfl.dflash_profile_enable(False)
     _log("[bench] kernels " + ", ".join(f"{k}={v['avg_us']:.1f}us" for k, v in kern.items()))
 
+    # plain streaming read of the same buffers: the measured read ceiling
+    read_gbps = None
+    if args.read_probe:
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        evs, nbytes = [], 0
+        for p in range(args.read_probe):
+            for dv in devs:
+                for buf in (dv["U"], dv["Z"]):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    dfl.dflash_read_probe(buf, sink)
+                    e1.record()
+                    if p:  # first pass warms up
+                        evs.append((e0, e1))
+                        nbytes += buf.numel() * buf.element_size()
+        torch.cuda.synchronize()
+        if evs:
+            read_gbps = nbytes / (sum(a.elapsed_time(b) for a, b in evs) * 1e-3) / 1e9
+            _log(f"[bench] read ceiling {read_gbps:.1f} GB/s")
+
     # the streaming launch reads every drafter and target logit once
     algo = {"cycle_stream": ub + zb}
     dom = max(algo, key=lambda k: kern.get(k, {}).get("avg_us", 0.0))
-    achieved = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
-    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(dom),
-            "algorithmic_bytes_per_launch": algo[dom]}
+    achieved = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9 if dom in kern else None
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+            "traffic": load_traffic(dom, base["name"]), "algorithmic_bytes_per_launch": algo[dom]}
     per_kernel_roof = {k: round(algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1) for k in algo if k in kern}
 
     cpu = None
@@ -198,6 +248,8 @@ def main():
         "logit_frac_of_peak": round(logit_gbps / HBM_PEAK_GBPS, 4),
         "roofline": roof,
         "kernel_GBps": per_kernel_roof,
+        "read_ceiling_GBps": round(read_gbps, 1) if read_gbps else None,
+        "frac_of_read_ceiling": round(achieved / read_gbps, 4) if (read_gbps and achieved) else None,
         "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "mean_accept_len": round(mean_accept, 3),
         "cpu_baseline": cpu,

@@ -4,7 +4,7 @@ Every function here checks tensor placement, dtype and contiguity, turns
 tensors into raw device pointers and calls the C ABI of the same name
 (``include/dflash.h``) on the current HIP stream.  All arithmetic of the path
 runs in the library's HIP kernels.  Importing this package fails if the
-library has not been built (``python -m block_draft_select_amd.build``).
+library has not been built (``python block_draft_select_amd/build.py``).
 """
 
 import ctypes
@@ -41,7 +41,7 @@ class DFlashError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_draft_select_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python block_draft_select_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
     D = ctypes.POINTER(dflash_dims)

@@ -1,6 +1,7 @@
 """Build libdflash.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m block_draft_select_amd.build`` (or ``build()`` from Python).
+Usage: ``python block_draft_select_amd/build.py`` (run by path: importing the
+package needs the built library), or ``__graft_entry__.build()``.
 Every source is compiled on each call; objects go to ``_build/`` next to this
 file and the library to ``block_draft_select_amd/libdflash.so``.
 """

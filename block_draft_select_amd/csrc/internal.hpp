@@ -28,7 +28,7 @@ constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
 
 struct ChunkStat {
   float m;      // chunk maximum logit
-  float s;      // sum over non-candidates of exp((z - m) / T)  (sampling rows)
+  float s;      // sum over the chunk of exp((z - m) / T)  (sampling rows)
   int32_t arg;  // first index of the maximum (greedy rows)
   int32_t pad;
 };

@@ -27,8 +27,10 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     const uint4 a = p[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
-  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
-  if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+  // The store depends on every loaded word, so no load can be dropped, but
+  // it happens (practically) never: a per-wave atomic would serialise the
+  // waves on one address and measure the atomic unit instead of HBM.
+  if (acc == 0x9E3779B9u) sink[0] = acc ^ (uint32_t)i;
 }
 
 __global__ __launch_bounds__(256) void copy_probe_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
