@@ -29,20 +29,28 @@ union StreamLds {
 template <int DT, int PT>
 __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U, const void* __restrict__ Z,
                                                      const void* __restrict__ h, const void* __restrict__ W, int R,
-                                                     int H, int r, float* __restrict__ g, int n_gate, int gate_cols,
+                                                     int H, int r, float* __restrict__ gpart, int n_gate, int gate_cols,
+                                                     int n_ks,
                                                      int V, int K, int L, int n_sub, int spb, int n_seg,
                                                      uint64_t* __restrict__ partial, int n_chunk, int n_grp,
                                                      const float* __restrict__ T, ChunkStat* __restrict__ stats) {
   __shared__ StreamLds sh;
   int id = blockIdx.x;
   if (id < n_gate) {
-    if (PT == DFLASH_BF16)
-      gate_tile_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, g,
-                     id / gate_cols, id - (id / gate_cols) * gate_cols, sh.red);
-    else
-      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, g, id);
+    if (PT == DFLASH_BF16) {
+      // id -> (row tile, column tile, hidden slice), slice fastest
+      const int ks = id % n_ks, tile = id / n_ks;
+      gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
+                        tile / gate_cols, tile - (tile / gate_cols) * gate_cols, ks, sh.red);
+    } else {
+      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, gpart, id);
+    }
     return;
   }
+  // top-K blocks in drafter-row order, then statistics blocks in target-row
+  // order: the whole grid sweeps U and then Z front to back (measured ~10%
+  // faster than interleaving the two kinds, which splits the reads between
+  // two distant regions)
   id -= n_gate;
   const int n_topk = R * n_seg;
   if (id < n_topk) {
@@ -69,7 +77,8 @@ struct CandLds {
 template <int DT, int PT>
 __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __restrict__ partial, int n_seg,
                                                           const int32_t* __restrict__ x0, const void* __restrict__ E,
-                                                          const float* __restrict__ g, const void* __restrict__ Z,
+                                                          const float* __restrict__ gpart, int n_ks,
+                                                          const void* __restrict__ Z,
                                                           int L, int V, int K, int r, int32_t* __restrict__ cand_idx,
                                                           float* __restrict__ cand_logit, float* __restrict__ zc,
                                                           float* __restrict__ S) {
@@ -90,10 +99,6 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
       const size_t o = (size_t)bt * K + tid;
       cand_idx[o] = c;
       cand_logit[o] = v;
-      const size_t zi = ((size_t)b * (L + 1) + t) * V + c;
-      zc[o] = DT == DFLASH_BF16
-                  ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
-                  : reinterpret_cast<const float*>(Z)[zi];
     } else if (t == 0) {
       p = clamp_idx(x0[b], V);
     }
@@ -102,7 +107,15 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
     cl.e.cl[tid] = v;
   }
   __syncthreads();
-  edge_scores<PT>(cl.e, E, g + (size_t)bt * r, K, r, S + (size_t)bt * K * K);
+  // the candidates' target logits are gathered while the embedding rows load
+  float zv = 0.f;
+  if (tid < K) {
+    const size_t zi = ((size_t)b * (L + 1) + t) * V + cl.e.cidx[tid];
+    zv = DT == DFLASH_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
+                           : reinterpret_cast<const float*>(Z)[zi];
+  }
+  edge_scores<PT>(cl.e, E, gpart, n_ks, (size_t)gridDim.x * r, bt, K, r, S + (size_t)bt * K * K);
+  if (tid < K) zc[(size_t)bt * K + tid] = zv;
 }
 
 template <int DT>
@@ -123,7 +136,8 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
                                const void* W_g, const float* T, char* ws, hipStream_t st) {
   const int R = d.B * d.L;
   const int gate_cols = (d.r + 63) / 64;
-  const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols : R;
+  const int n_ks = gate_slices(d);
+  const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols * n_ks : R;
   const int n_grp = (w.n_chunk + 3) / 4;
   const long long blocks = (long long)n_gate + (long long)R * w.n_seg + (long long)d.B * (d.L + 1) * n_grp;
   float* g = reinterpret_cast<float*>(ws + w.gate);
@@ -131,8 +145,8 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
   ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws + w.stats);
 #define DF_STREAM(DT, PT)                                                                                     \
   hipLaunchKernelGGL((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), 0, st, U, Z, h, W_g, R,      \
-                     d.hidden, d.r, g, n_gate, gate_cols, d.V, d.K, d.L, w.n_sub, w.spb, w.n_seg, partial,     \
-                     w.n_chunk, n_grp, T, stats)
+                     d.hidden, d.r, g, n_gate, gate_cols, n_ks, d.V, d.K, d.L, w.n_sub, w.spb, w.n_seg,        \
+                     partial, w.n_chunk, n_grp, T, stats)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_STREAM(DFLASH_BF16, DFLASH_BF16); else DF_STREAM(DFLASH_BF16, DFLASH_F32);
   } else {
@@ -150,8 +164,8 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
   const float* g = reinterpret_cast<const float*>(ws + w.gate);
   float* zc = reinterpret_cast<float*>(ws + w.zc);
 #define DF_SCORES(DT, PT)                                                                                      \
-  hipLaunchKernelGGL((cand_scores_kernel<DT, PT>), grid, dim3(256), 0, st, partial, w.n_seg, x0, E, g, Z, d.L, \
-                     d.V, d.K, d.r, cand_idx, cand_logit, zc, S)
+  hipLaunchKernelGGL((cand_scores_kernel<DT, PT>), grid, dim3(256), 0, st, partial, w.n_seg, x0, E, g,         \
+                     gate_slices(d), Z, d.L, d.V, d.K, d.r, cand_idx, cand_logit, zc, S)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);
   } else {

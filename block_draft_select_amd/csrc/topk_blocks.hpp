@@ -16,6 +16,9 @@
 //   2. values at or above the threshold are appended to an LDS buffer next
 //      to the running list and merged into it by exact rank (value desc,
 //      index asc).
+// Once a wave's running list is full, its K-th key + 1 replaces the
+// per-sub-segment threshold (later sub-segments have larger indices and
+// lose ties), and the bisection is skipped.
 // A tie-heavy sub-segment whose candidates overflow the buffer takes an
 // out-of-line exact path that re-reads it.  A block (4 waves) owns a run of
 // sub-segments and writes the sorted top list of that run; the lists of a
@@ -50,33 +53,58 @@ __device__ __forceinline__ int count_greater(const uint64_t* list, int n, uint64
   return lo;
 }
 
+// number of entries of a 16-entry descending list (zeros last) greater
+// than key: 16 independent loads and compares, no dependent chain
+__device__ __forceinline__ int count_greater16(const uint64_t* list, uint64_t key) {
+  int n = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) n += list[k] > key ? 1 : 0;
+  return n;
+}
+
 // Merge the buffered keys into the running list.  buf[0, ntop) is the
 // running list (sorted, descending); buf[ntop, cnt) holds new candidates in
 // any order; all keys are distinct and non-zero.  A running key's new rank
 // is its position plus the number of larger new keys; a new key's rank is
 // the number of larger running keys (binary search) plus larger new keys.
-__device__ void merge_buffer(TkWave& w, int K, int lane) {
+__device__ void merge_buffer(TkWave& w, uint32_t cnt, int K, int lane) {
   const uint32_t ntop = w.ntop;
-  const uint32_t c = min(w.cnt, (uint32_t)kTopkCap);
+  const uint32_t c = min(cnt, (uint32_t)kTopkCap);
   if (c == ntop) return;  // nothing new
-  uint64_t mine[(kTopkCap + 16) / kWave + 1];
-  uint32_t rank[(kTopkCap + 16) / kWave + 1];
-  constexpr int SL = (kTopkCap + 16) / kWave + 1;
+  if (c <= (uint32_t)kWave) {
+    // one key per lane: its rank is the number of larger keys among all c,
+    // read in batches of 16 independent loads
+    const uint64_t mine = lane < (int)c ? w.buf[lane] : 0ull;
+    uint32_t rank = 0;
+    for (uint32_t j0 = 0; j0 < c; j0 += 16) {
+      uint64_t o[16];
 #pragma unroll
-  for (int s = 0; s < SL; ++s) {
-    const uint32_t i = lane + s * kWave;
-    mine[s] = i < c ? w.buf[i] : 0ull;
-    rank[s] = i < ntop ? i : (i < c ? (uint32_t)count_greater(w.buf, (int)ntop, mine[s]) : 0xFFFFu);
+      for (int u = 0; u < 16; ++u) o[u] = w.buf[j0 + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) rank += (j0 + u < c && o[u] > mine) ? 1u : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < (int)c && rank < (uint32_t)K) w.top[rank] = mine;
+  } else {
+    constexpr int SL = (kTopkCap + 16) / kWave + 1;
+    uint64_t mine[SL];
+    uint32_t rank[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint32_t i = lane + s * kWave;
+      mine[s] = i < c ? w.buf[i] : 0ull;
+      rank[s] = i < ntop ? i : (i < c ? (uint32_t)count_greater(w.buf, (int)ntop, mine[s]) : 0xFFFFu);
+    }
+    for (uint32_t j = ntop; j < c; ++j) {
+      const uint64_t o = w.buf[j];
+#pragma unroll
+      for (int s = 0; s < SL; ++s) rank[s] += (o > mine[s]) ? 1u : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      if (mine[s] != 0ull && rank[s] < (uint32_t)K) w.top[rank[s]] = mine[s];
   }
-  for (uint32_t j = ntop; j < c; ++j) {
-    const uint64_t o = w.buf[j];
-#pragma unroll
-    for (int s = 0; s < SL; ++s) rank[s] += (o > mine[s]) ? 1u : 0u;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-  for (int s = 0; s < SL; ++s)
-    if (mine[s] != 0ull && rank[s] < (uint32_t)K) w.top[rank[s]] = mine[s];
   if (lane == 0) w.ntop = min(c, (uint32_t)K);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
@@ -157,18 +185,29 @@ __device__ __forceinline__ uint32_t max_i16x2(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(s16x2, b)));
 }
 
-// append the candidates of one register (two bf16 patterns) whose 16-bit
-// ordered key is >= thr
-__device__ __forceinline__ void collect_pair(uint32_t raw, int idx0, uint32_t thr, TkWave& w) {
-  const uint32_t k2 = ord16x2(raw);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t k16 = h ? (k2 >> 16) : (k2 & 0xFFFFu);
-    if (k16 >= thr) {
-      const uint32_t pos = atomicAdd(&w.cnt, 1u);
-      if (pos < (uint32_t)kTopkCap) w.buf[pos] = make_key(ord32_of_k16(k16), (uint32_t)(idx0 + h));
-    }
+// number of set bits of ballot b held by lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Append `key` from every lane where `hit` holds, after the first `cnt`
+// buffer entries (cnt is the same in every lane): a lane's slot is the
+// number of hitting lanes below it, so no atomic and no round trip.
+__device__ __forceinline__ void append_hits(bool hit, uint64_t key, TkWave& w, uint32_t& cnt) {
+  const uint64_t b = __ballot(hit);
+  if (hit) {
+    const uint32_t pos = cnt + lanes_below(b);
+    if (pos < (uint32_t)kTopkCap) w.buf[pos] = key;
   }
+  cnt += (uint32_t)__popcll(b);
+}
+
+// append both bf16 values of one register whose 16-bit ordered key >= thr
+__device__ __forceinline__ void append_pair(uint32_t raw, int idx0, uint32_t thr, TkWave& w, uint32_t& cnt) {
+  const uint32_t k2 = ord16x2(raw);
+  const uint32_t klo = k2 & 0xFFFFu, khi = k2 >> 16;
+  append_hits(klo >= thr, make_key(ord32_of_k16(klo), (uint32_t)idx0), w, cnt);
+  append_hits(khi >= thr, make_key(ord32_of_k16(khi), (uint32_t)(idx0 + 1)), w, cnt);
 }
 
 // Fold bf16 sub-segment [lo, hi) of `row` into the wave's running list.
@@ -179,122 +218,119 @@ __device__ __forceinline__ void collect_pair(uint32_t raw, int idx0, uint32_t th
 // when it is >= the threshold's pattern as a signed 16-bit integer, so the
 // candidate test needs no key transform.
 __device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
-  constexpr int WS = 64 * kTopkLoads * 8;
+  // 16-byte units lie wholly inside or outside [lo, hi) (row lengths are
+  // multiples of 8 values); units past hi hold 0xFFFF pairs (key 0: never
+  // admitted, and a lane whose pick is padding adds nothing to the count)
   uint32_t x[4 * kTopkLoads];
-  if (hi - lo == WS) {
 #pragma unroll
-    for (int j = 0; j < kTopkLoads; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 8);
-      x[4 * j + 0] = v.x;
-      x[4 * j + 1] = v.y;
-      x[4 * j + 2] = v.z;
-      x[4 * j + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kTopkLoads; ++j) {
-      const int base = lo + (j * kWave + lane) * 8;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t e0 = (base + 2 * c < hi) ? (uint32_t)row[base + 2 * c] : 0xFFFFu;
-        const uint32_t e1 = (base + 2 * c + 1 < hi) ? (uint32_t)row[base + 2 * c + 1] : 0xFFFFu;
-        x[4 * j + c] = e0 | (e1 << 16);  // 0xFFFF: key 0, never admitted
-      }
-    }
+  for (int j = 0; j < kTopkLoads; ++j) {
+    const int base = lo + (j * kWave + lane) * 8;
+    uint4 v = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    if (base < hi) v = load_stream16(row + base);
+    x[4 * j + 0] = v.x;
+    x[4 * j + 1] = v.y;
+    x[4 * j + 2] = v.z;
+    x[4 * j + 3] = v.w;
   }
-  uint32_t m = x[0];
-#pragma unroll
-  for (int q = 1; q < 4 * kTopkLoads; ++q) m = max_i16x2(m, x[q]);
-  const int pick = max((int)(int16_t)(m & 0xFFFFu), (int)(int16_t)(m >> 16));
-  const uint32_t pick_key = ord16x2((uint32_t)pick & 0xFFFFu) & 0xFFFFu;
-
-  // K-th largest pick
-  uint32_t thr = 0;
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t c = thr | (1u << bit);
-    if (__popcll(__ballot(pick_key >= c)) >= (unsigned)K) thr = c;
-  }
-  if (thr == 0x8000u) thr = 0x7FFFu;  // a +0.0 threshold also admits -0.0
-  if (thr == 0u) thr = 1u;            // never admit padding
   const uint32_t ntop = w.ntop;
-  if (ntop == (uint32_t)K) thr = max(thr, (uint32_t)(w.top[K - 1] >> 48) + 1u);
+  uint32_t thr;
+  if (ntop == (uint32_t)K) {
+    thr = (uint32_t)(w.top[K - 1] >> 48) + 1u;
+  } else {
+    uint32_t m = x[0];
+#pragma unroll
+    for (int q = 1; q < 4 * kTopkLoads; ++q) m = max_i16x2(m, x[q]);
+    const int pick = max((int)(int16_t)(m & 0xFFFFu), (int)(int16_t)(m >> 16));
+    const uint32_t pick_key = ord16x2((uint32_t)pick & 0xFFFFu) & 0xFFFFu;
+    // K-th largest pick
+    thr = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      if (__popcll(__ballot(pick_key >= c)) >= (unsigned)K) thr = c;
+    }
+    if (thr == 0x8000u) thr = 0x7FFFu;  // a +0.0 threshold also admits -0.0
+    if (thr == 0u) thr = 1u;            // never admit padding
+  }
 
-  // buffer = running list, then the new candidates
+  // buffer = running list, then the new candidates; a register is looked
+  // at closely only when some lane's register passes the packed test
   if (lane < (int)ntop) w.buf[lane] = w.top[lane];
-  if (lane == 0) w.cnt = ntop;
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  uint32_t cnt = ntop;
   if (thr > 0x8000u && thr <= 0xFFFFu) {
     const uint32_t tm1 = ((thr & 0x7FFFu) - 1u) * 0x00010001u;  // positive pattern - 1, both halves
 #pragma unroll
     for (int q = 0; q < 4 * kTopkLoads; ++q)
-      if (max_i16x2(x[q], tm1) != tm1)
-        collect_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w);
+      if (__ballot(max_i16x2(x[q], tm1) != tm1))
+        append_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w, cnt);
   } else if (thr <= 0xFFFFu) {
     const uint32_t tm1 = (thr - 1u) * 0x00010001u;
 #pragma unroll
     for (int q = 0; q < 4 * kTopkLoads; ++q)
-      if (subsat_u16x2(ord16x2(x[q]), tm1) != 0u)
-        collect_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w);
+      if (__ballot(subsat_u16x2(ord16x2(x[q]), tm1) != 0u))
+        append_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w, cnt);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (w.cnt > (uint32_t)kTopkCap) exact_subsegment<DFLASH_BF16>(row, lo, hi, K, lane, w, ntop);
-  merge_buffer(w, K, lane);
+  if (cnt > (uint32_t)kTopkCap) {
+    exact_subsegment<DFLASH_BF16>(row, lo, hi, K, lane, w, ntop);
+    cnt = w.cnt;
+  }
+  merge_buffer(w, cnt, K, lane);
 }
 
 // fold fp32 sub-segment [lo, hi) of `row` into the wave's running list
 __device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
-  constexpr int WS = 64 * kTopkLoads * 4;
+  // units past hi hold key 0 (never admitted)
   uint32_t kx[4 * kTopkLoads];
-  if (hi - lo == WS) {
 #pragma unroll
-    for (int j = 0; j < kTopkLoads; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row + lo + (j * kWave + lane) * 4);
-      kx[4 * j + 0] = ord32(v.x);
-      kx[4 * j + 1] = ord32(v.y);
-      kx[4 * j + 2] = ord32(v.z);
-      kx[4 * j + 3] = ord32(v.w);
+  for (int j = 0; j < kTopkLoads; ++j) {
+    const int base = lo + (j * kWave + lane) * 4;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (base < hi) {
+      v = load_stream16(row + base);
+      v = make_uint4(ord32(v.x), ord32(v.y), ord32(v.z), ord32(v.w));
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kTopkLoads; ++j) {
-      const int base = lo + (j * kWave + lane) * 4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kx[4 * j + c] = (base + c < hi) ? ord32(row[base + c]) : 0u;
-    }
+    kx[4 * j + 0] = v.x;
+    kx[4 * j + 1] = v.y;
+    kx[4 * j + 2] = v.z;
+    kx[4 * j + 3] = v.w;
   }
-  uint32_t lanemax = kx[0];
-#pragma unroll
-  for (int q = 1; q < 4 * kTopkLoads; ++q) lanemax = max(lanemax, kx[q]);
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = thr | (1u << bit);
-    if (__popcll(__ballot(lanemax >= c)) >= (unsigned)K) thr = c;
-  }
-  if (thr == 0x80000000u) thr = 0x7FFFFFFFu;
-  if (thr == 0u) thr = 1u;
   const uint32_t ntop = w.ntop;
+  uint32_t thr;
   bool none = false;
   if (ntop == (uint32_t)K) {
     const uint32_t t = (uint32_t)(w.top[K - 1] >> 32);
-    if (t == 0xFFFFFFFFu) none = true; else thr = max(thr, t + 1u);
+    if (t == 0xFFFFFFFFu) none = true;
+    thr = t + 1u;
+  } else {
+    uint32_t lanemax = kx[0];
+#pragma unroll
+    for (int q = 1; q < 4 * kTopkLoads; ++q) lanemax = max(lanemax, kx[q]);
+    thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      if (__popcll(__ballot(lanemax >= c)) >= (unsigned)K) thr = c;
+    }
+    if (thr == 0x80000000u) thr = 0x7FFFFFFFu;
+    if (thr == 0u) thr = 1u;
   }
   if (lane < (int)ntop) w.buf[lane] = w.top[lane];
-  if (lane == 0) w.cnt = ntop;
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  uint32_t cnt = ntop;
   if (!none) {
 #pragma unroll
     for (int q = 0; q < 4 * kTopkLoads; ++q) {
-      if (kx[q] >= thr) {
+      if (__ballot(kx[q] >= thr)) {
         const uint32_t canon = kx[q] == 0x7FFFFFFFu ? 0x80000000u : kx[q];
         const int idx = lo + ((q >> 2) * kWave + lane) * 4 + (q & 3);
-        const uint32_t pos = atomicAdd(&w.cnt, 1u);
-        if (pos < (uint32_t)kTopkCap) w.buf[pos] = make_key(canon, (uint32_t)idx);
+        append_hits(kx[q] >= thr, make_key(canon, (uint32_t)idx), w, cnt);
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (w.cnt > (uint32_t)kTopkCap) exact_subsegment<DFLASH_F32>(row, lo, hi, K, lane, w, ntop);
-  merge_buffer(w, K, lane);
+  if (cnt > (uint32_t)kTopkCap) {
+    exact_subsegment<DFLASH_F32>(row, lo, hi, K, lane, w, ntop);
+    cnt = w.cnt;
+  }
+  merge_buffer(w, cnt, K, lane);
 }
 
 
@@ -329,7 +365,7 @@ __device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, in
       int rank = k;
 #pragma unroll
       for (int o = 0; o < 4; ++o)
-        if (o != lw) rank += count_greater(sw[o].top, K, key);
+        if (o != lw) rank += count_greater16(sw[o].top, key);
       if (rank < K) block_top[rank] = key;
     }
   }
@@ -353,7 +389,7 @@ __device__ __forceinline__ void merge_row(const uint64_t* __restrict__ lists, in
     if (key == 0ull || k >= K) continue;
     int rank = k;
     for (int s2 = 0; s2 < n_seg && rank < K; ++s2)
-      if (s2 != s) rank += count_greater(keys + s2 * 16, K, key);
+      if (s2 != s) rank += count_greater16(keys + s2 * 16, key);
     if (rank < K) out[rank] = key;
   }
   __syncthreads();
@@ -379,7 +415,7 @@ __device__ __forceinline__ void merge_two_rows(const uint64_t* __restrict__ list
     const uint64_t* base = keys + half * nk;
     int rank = k;
     for (int s2 = 0; s2 < n_seg && rank < K; ++s2)
-      if (s2 != s) rank += count_greater(base + s2 * 16, K, key);
+      if (s2 != s) rank += count_greater16(base + s2 * 16, key);
     if (rank < K) (half ? out1 : out0)[rank] = key;
   }
   __syncthreads();
