@@ -22,6 +22,7 @@ union StreamLds {
   struct {
     TkWave sw[4];
     uint64_t block_top[16];
+    uint32_t bound;
   } tk;
   float red[kGateRed];
 };
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U,
   const int n_topk = R * n_seg;
   if (id < n_topk) {
     const int row = id / n_seg, seg = id - row * n_seg;
-    topk_block<DT>(U, V, K, n_sub, spb, row, seg, sh.tk.sw, sh.tk.block_top,
+    topk_block<DT>(U, V, K, n_sub, spb, row, seg, sh.tk.sw, sh.tk.block_top, &sh.tk.bound,
                    partial + ((size_t)row * n_seg + seg) * 16);
     return;
   }

@@ -273,38 +273,58 @@ __device__ __forceinline__ double group_last_f64(double v, int g) {
   return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
-// Four rows of the trace table at once (16-lane group g of the wave takes
-// row row0 + g): row (t, i) holds the scores S[t][i][.] of the successors
-// of rank i at position t (LDS, K floats).  Each row gets the walk's
-// decision -- the same arithmetic as trace_step_dpp -- written to
+// NQ x 4 rows of the trace table at once (16-lane group g of the wave takes
+// rows row0 + 4 n + g, n < NQ; the NQ quads are independent, so their
+// latency chains overlap): row (t, i) holds the scores S[t][i][.] of the
+// successors of rank i at position t (LDS, K floats).  Each row gets the
+// walk's decision -- the same arithmetic as trace_step_dpp -- written to
 // jstar[row], and its q written over the scores in place.  With every row
 // decided up front, the sequential walk is only L table look-ups.
 // u[t] holds the trace uniform of position t (unused when greedy).
-__device__ __forceinline__ void trace_rows4(float* S, int row0, int n_rows, int K, float Tb, double invT,
-                                            const uint4* u, int* jstar, int lane) {
+template <int NQ>
+__device__ __forceinline__ void trace_rows(float* S, int row0, int n_rows, int K, float Tb, double invT,
+                                           const uint4* u, int* jstar, int lane) {
   const int g = lane >> 4, j = lane & 15;
-  const int row = row0 + g;
-  const bool live = row < n_rows && j < K;
-  float* srow = S + (size_t)(row < n_rows ? row : 0) * K;
-  const float s = live ? srow[j] : -INFINITY;
-  const float m = __uint_as_float(group_last_u32(__float_as_uint(row16_scan_max_f32(s)), g));
-  int jd;
-  float qv;
-  if (!(Tb > 0.0f)) {
-    const uint32_t bits = (uint32_t)(__ballot(live && s == m) >> (16 * g)) & 0xFFFFu;
-    jd = bits ? __builtin_ctz(bits) : 0;
-    qv = j == jd ? 1.0f : 0.0f;
-  } else {
-    const double w = live ? exp_nonpos(((double)s - (double)m) * invT) : 0.0;
-    const double cum = row16_scan_f64(w);
-    const double total = group_last_f64(cum, g);
-    const double target = (double)u01_f32(u[row < n_rows ? row / K : 0].x) * total;
-    const uint32_t bits = (uint32_t)(__ballot(live && cum > target) >> (16 * g)) & 0xFFFFu;
-    jd = bits ? __builtin_ctz(bits) : K - 1;
-    qv = (float)(w / total);
+  int row[NQ];
+  bool live[NQ];
+  float s[NQ], m[NQ];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    row[n] = row0 + 4 * n + g;
+    live[n] = row[n] < n_rows && j < K;
+    s[n] = live[n] ? S[(size_t)row[n] * K + j] : -INFINITY;
   }
-  if (live) srow[j] = qv;
-  if (row < n_rows && j == 0) jstar[row] = jd;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) m[n] = __uint_as_float(group_last_u32(__float_as_uint(row16_scan_max_f32(s[n])), g));
+  int jd[NQ];
+  float qv[NQ];
+  if (!(Tb > 0.0f)) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const uint32_t bits = (uint32_t)(__ballot(live[n] && s[n] == m[n]) >> (16 * g)) & 0xFFFFu;
+      jd[n] = bits ? __builtin_ctz(bits) : 0;
+      qv[n] = j == jd[n] ? 1.0f : 0.0f;
+    }
+  } else {
+    double w[NQ], cum[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) w[n] = live[n] ? exp_nonpos(((double)s[n] - (double)m[n]) * invT) : 0.0;
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) cum[n] = row16_scan_f64(w[n]);
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const double total = group_last_f64(cum[n], g);
+      const double target = (double)u01_f32(u[row[n] < n_rows ? row[n] / K : 0].x) * total;
+      const uint32_t bits = (uint32_t)(__ballot(live[n] && cum[n] > target) >> (16 * g)) & 0xFFFFu;
+      jd[n] = bits ? __builtin_ctz(bits) : K - 1;
+      qv[n] = (float)(w[n] / total);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    if (live[n]) S[(size_t)row[n] * K + j] = qv[n];
+    if (row[n] < n_rows && j == 0) jstar[row[n]] = jd[n];
+  }
 }
 
 }  // namespace dfk

@@ -188,7 +188,6 @@ __device__ __forceinline__ void load_tokens(const void* __restrict__ Z, size_t z
 constexpr int kFinThreads = 1024;  // 16 waves: the parallel phases split 16 ways
 constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kFinTpt = kChunk / kFinThreads;  // tokens per thread in the in-chunk draw
-constexpr int kMaxChunks = DFLASH_V_MAX / kChunk;
 constexpr int kTermCache = 2048;  // chunk terms of all rows kept in LDS when they fit
 
 struct FinLds {
@@ -206,9 +205,9 @@ struct FinLds {
   int rank[DFLASH_L_MAX];
   uint4 rnd0[DFLASH_L_MAX];                         // (cycle, t + 1, 0) blocks
   uint4 rnd1[DFLASH_L_MAX + 1];                     // (cycle, t + 1, 1) blocks
-  double item[kMaxChunks + DFLASH_K_MAX];
+  int pick_row[DFLASH_L_MAX + 1];                   // first-level draw of every row
   double wave_tot[kFinWaves];
-  int s_n, s_pick, s_tok, s_last;
+  int s_n, s_tok, s_last;
 };
 
 // Combine the statistics of row t (one wave): maximum, first argmax chunk,
@@ -246,6 +245,73 @@ __device__ __forceinline__ void combine_row(FinLds& f, const ChunkStat* __restri
     f.rowM[t] = M;
     f.rowAll[t] = s;
   }
+}
+
+// First level of the residual/bonus draw of row t (one wave, registers
+// only): the index of the drawn item among [chunk 0 .. n_chunk - 1 (the
+// chunk's mass without the row's candidates), candidate 0 .. nk - 1
+// (max(0, p - q))], nk = K for t < L and 0 for the bonus row.  If the
+// residual has no mass the candidates keep mass p instead.  Items past the
+// first 64 are recomputed in a second pass rather than stored.
+__device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __restrict__ st, int t, int L, int K,
+                                         int n_chunk, bool cached, double invT, int lane) {
+  const int nk = t < L ? K : 0;
+  const double inv = 1.0 / f.rowAll[t];
+  const uint4 w1 = f.rnd1[t];
+  // the row's candidates in registers: their chunk and weight
+  int cchunk[DFLASH_K_MAX];
+  double cpc[DFLASH_K_MAX];
+#pragma unroll
+  for (int k = 0; k < DFLASH_K_MAX; ++k) {
+    cchunk[k] = k < nk ? f.cand[t][k] / kChunk : -1;
+    cpc[k] = k < nk ? f.pc[t][k] : 0.0;
+  }
+  const int n_item = n_chunk + nk;
+  auto item = [&](int i, bool resid) -> double {
+    if (i < n_chunk) {
+      double tm;
+      if (cached) {
+        tm = f.term[t * n_chunk + i];
+      } else {
+        const ChunkStat cs = st[i];
+        tm = (double)cs.s * exp_nonpos(((double)cs.m - (double)f.rowM[t]) * invT);
+      }
+      double cm = 0.0;
+#pragma unroll
+      for (int k = 0; k < DFLASH_K_MAX; ++k)
+        if (k < nk && cchunk[k] == i) cm += cpc[k];
+      return fmax(0.0, (tm - cm) * inv);
+    }
+    if (i < n_item) {
+      const double p = f.pc[t][i - n_chunk] * inv;
+      return resid ? fmax(0.0, p - (double)f.qs[t][i - n_chunk]) : p;
+    }
+    return 0.0;
+  };
+  bool resid = true;
+  double total = 0.0, cum0 = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    double carry = 0.0;
+    for (int base = 0; base < n_item; base += kWave) {
+      const double v = wave_scan_f64(item(base + lane, resid)) + carry;
+      if (base == 0) cum0 = v;
+      carry = readlane_f64(v, 63);
+    }
+    total = carry;
+    if (total > 0.0 || nk == 0 || !resid) break;
+    resid = false;  // the residual has no mass: draw from p itself
+  }
+  const double target = u01_f64(w1.x, w1.y) * total;
+  const int fl0 = first_lane(lane < n_item && cum0 > target);
+  if (fl0 < 64) return fl0;
+  double carry = readlane_f64(cum0, 63);
+  for (int base = kWave; base < n_item; base += kWave) {
+    const double v = wave_scan_f64(item(base + lane, resid)) + carry;
+    const int fl = first_lane(base + lane < n_item && v > target);
+    if (fl < 64) return base + fl;
+    carry = readlane_f64(v, 63);
+  }
+  return n_item - 1;
 }
 
 // One block per stream.  WITH_TRACE: the block also walks the trace over
@@ -311,16 +377,17 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   }
   __syncthreads();
 
-  // (1) the trace table (every row's decision, four rows per wave step)
-  // and the per-row combination, spread over the four waves
+  // (1) the trace table (every row's decision, eight rows per wave task)
+  // and the per-row combination (one wave task per target row), spread over
+  // the waves
   {
     const int n_rows = WITH_TRACE ? L * K : 0;
-    const int n_quads = (n_rows + 3) / 4;
-    for (int task = wave; task < n_quads + L + 1; task += kFinWaves) {
-      if (task < n_quads)
-        trace_rows4(f.S, task * 4, n_rows, K, Tb, invT, f.rnd0, f.jstar, lane);
+    const int n_oct = (n_rows + 7) / 8;
+    for (int task = wave; task < n_oct + L + 1; task += kFinWaves) {
+      if (task < n_oct)
+        trace_rows<2>(f.S, task * 8, n_rows, K, Tb, invT, f.rnd0, f.jstar, lane);
       else
-        combine_row<DT>(f, st_all + (size_t)(task - n_quads) * n_chunk, task - n_quads, L, K, n_chunk, cached,
+        combine_row<DT>(f, st_all + (size_t)(task - n_oct) * n_chunk, task - n_oct, L, K, n_chunk, cached,
                         greedy, invT, lane);
     }
   }
@@ -363,6 +430,8 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   }
 
   // (2) accept tests, all positions at once: u_t * q_t(d_t) < p_t(d_t)
+  // (wave 0), beside the first level of the residual/bonus draw for every
+  // row that could be the sampling row (the other waves, one row each)
   if (wave == 0) {
     bool rejected = false;
     if (lane < L) {
@@ -372,77 +441,15 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       rejected = !(u * (double)f.qs[lane][j] < p);
     }
     const int fl = first_lane(rejected);
-    const int ts = fl < L ? fl : L;
-    if (lane == 0) f.s_n = ts;
-    const int nk = ts < L ? K : 0;
-    const double inv = 1.0 / f.rowAll[ts];
-    const uint4 w1 = f.rnd1[ts];
-    const ChunkStat* st = st_all + (size_t)ts * n_chunk;
-
-    // (3) residual items of row ts (the same wave, no barrier): chunk masses
-    // without the candidates, then the candidates' max(0, p - q)
-    // the row's candidates in registers: their chunk and weight
-    int cchunk[DFLASH_K_MAX];
-    double cpc[DFLASH_K_MAX];
-#pragma unroll
-    for (int k = 0; k < DFLASH_K_MAX; ++k) {
-      cchunk[k] = k < nk ? f.cand[ts][k] / kChunk : -1;
-      cpc[k] = k < nk ? f.pc[ts][k] : 0.0;
-    }
-    const int n_item = n_chunk + nk;
-    bool resid = true;
-    double total = 0.0;
-    double cum0 = 0.0;  // inclusive prefix of items 0..63 (lane i: item i)
-    for (int pass = 0; pass < 2; ++pass) {
-      double carry = 0.0;
-      for (int base = 0; base < n_item; base += kWave) {
-        const int i = base + lane;
-        double v = 0.0;
-        if (i < n_chunk) {
-          double tm;
-          if (cached) {
-            tm = f.term[ts * n_chunk + i];
-          } else {
-            const ChunkStat cs = st[i];
-            tm = (double)cs.s * exp_nonpos(((double)cs.m - (double)f.rowM[ts]) * invT);
-          }
-          double cm = 0.0;
-#pragma unroll
-          for (int k = 0; k < DFLASH_K_MAX; ++k)
-            if (k < nk && cchunk[k] == i) cm += cpc[k];
-          v = fmax(0.0, (tm - cm) * inv);
-        } else if (i < n_item) {
-          const double p = f.pc[ts][i - n_chunk] * inv;
-          v = resid ? fmax(0.0, p - (double)f.qs[ts][i - n_chunk]) : p;
-        }
-        v = wave_scan_f64(v) + carry;
-        if (base == 0) cum0 = v;
-        else if (i < n_item) f.item[i] = v;
-        carry = readlane_f64(v, 63);
-      }
-      total = carry;
-      if (total > 0.0 || nk == 0 || !resid) break;
-      resid = false;  // the residual has no mass: draw from p itself (candidates keep mass p)
-    }
-    const double target = u01_f64(w1.x, w1.y) * total;
-    int pick = n_item - 1;
-    const int fl0 = first_lane(lane < n_item && cum0 > target);  // the first 64 items stay in registers
-    if (fl0 < 64) {
-      pick = fl0;
-    } else {
-      for (int base = kWave; base < n_item; base += kWave) {
-        const int i = base + lane;
-        const int fl = first_lane(i < n_item && f.item[i] > target);
-        if (fl < 64) {
-          pick = base + fl;
-          break;
-        }
-      }
-    }
     if (lane == 0) {
-      f.s_pick = pick;
+      f.s_n = fl < L ? fl : L;
       f.s_tok = 0x7FFFFFFF;
       f.s_last = -1;
+    }
+  } else {
+    for (int t = wave - 1; t <= L; t += kFinWaves - 1) {
+      const int pk = pick_item(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, invT, lane);
+      if (lane == 0) f.pick_row[t] = pk;
     }
   }
   __syncthreads();
@@ -450,7 +457,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   const int nk = ts < L ? K : 0;
   const uint4 w1 = f.rnd1[ts];
   const ChunkStat* st = st_all + (size_t)ts * n_chunk;
-  const int pick = f.s_pick;
+  const int pick = f.pick_row[ts];
   int tok;
   if (pick >= n_chunk) {
     tok = f.cand[ts][pick - n_chunk];

@@ -16,8 +16,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(const void* 
                                                                     uint64_t* __restrict__ partial) {
   __shared__ TkWave sw[4];
   __shared__ uint64_t block_top[16];
+  __shared__ uint32_t bound;
   const int row = blockIdx.y, seg = blockIdx.x;
-  topk_block<DT>(U, V, K, n_sub, spb, row, seg, sw, block_top,
+  topk_block<DT>(U, V, K, n_sub, spb, row, seg, sw, block_top, &bound,
                  partial + ((size_t)row * gridDim.x + seg) * 16);
 }
 

@@ -18,7 +18,10 @@
 //      index asc).
 // Once a wave's running list is full, its K-th key + 1 replaces the
 // per-sub-segment threshold (later sub-segments have larger indices and
-// lose ties), and the bisection is skipped.
+// lose ties), and the bisection is skipped.  The four waves of a block also
+// share a lower bound in LDS: any wave's K-th value bounds the block's K-th
+// value from below, so smaller values cannot be in the block's list (equal
+// values still can, by index).
 // A tie-heavy sub-segment whose candidates overflow the buffer takes an
 // out-of-line exact path that re-reads it.  A block (4 waves) owns a run of
 // sub-segments and writes the sorted top list of that run; the lists of a
@@ -217,7 +220,8 @@ __device__ __forceinline__ void append_pair(uint32_t raw, int idx0, uint32_t thr
 // threshold.  When the threshold is positive, a raw pattern passes exactly
 // when it is >= the threshold's pattern as a signed 16-bit integer, so the
 // candidate test needs no key transform.
-__device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
+__device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane,
+                               uint32_t* bbound) {
   // 16-byte units lie wholly inside or outside [lo, hi) (row lengths are
   // multiples of 8 values); units past hi hold 0xFFFF pairs (key 0: never
   // admitted, and a lane whose pick is padding adds nothing to the count)
@@ -251,6 +255,9 @@ __device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi,
     if (thr == 0x8000u) thr = 0x7FFFu;  // a +0.0 threshold also admits -0.0
     if (thr == 0u) thr = 1u;            // never admit padding
   }
+  uint32_t sb = *bbound;                // 16-bit key of the block bound
+  if (sb == 0x8000u) sb = 0x7FFFu;      // a +0.0 bound also admits -0.0
+  thr = max(thr, sb);
 
   // buffer = running list, then the new candidates; a register is looked
   // at closely only when some lane's register passes the packed test
@@ -275,10 +282,12 @@ __device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi,
     cnt = w.cnt;
   }
   merge_buffer(w, cnt, K, lane);
+  if (lane == 0 && w.ntop == (uint32_t)K) atomicMax(bbound, (uint32_t)(w.top[K - 1] >> 48));
 }
 
 // fold fp32 sub-segment [lo, hi) of `row` into the wave's running list
-__device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane) {
+__device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane,
+                              uint32_t* bbound) {
   // units past hi hold key 0 (never admitted)
   uint32_t kx[4 * kTopkLoads];
 #pragma unroll
@@ -313,6 +322,9 @@ __device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, 
     if (thr == 0x80000000u) thr = 0x7FFFFFFFu;
     if (thr == 0u) thr = 1u;
   }
+  uint32_t sb = *bbound;                   // 32-bit key of the block bound
+  if (sb == 0x80000000u) sb = 0x7FFFFFFFu;  // a +0.0 bound also admits -0.0
+  thr = max(thr, sb);
   if (lane < (int)ntop) w.buf[lane] = w.top[lane];
   uint32_t cnt = ntop;
   if (!none) {
@@ -331,6 +343,7 @@ __device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, 
     cnt = w.cnt;
   }
   merge_buffer(w, cnt, K, lane);
+  if (lane == 0 && w.ntop == (uint32_t)K) atomicMax(bbound, (uint32_t)(w.top[K - 1] >> 32));
 }
 
 
@@ -340,20 +353,22 @@ __device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, 
 // waves, `block_top` 16 LDS keys.
 template <int DT>
 __device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, int K, int n_sub, int spb, int row,
-                                           int seg, TkWave* sw, uint64_t* block_top, uint64_t* __restrict__ out16) {
+                                           int seg, TkWave* sw, uint64_t* block_top, uint32_t* bbound,
+                                           uint64_t* __restrict__ out16) {
   constexpr int WS = 64 * kTopkLoads * (DT == DFLASH_BF16 ? 8 : 4);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   TkWave& w = sw[wave];
   if (lane < 16) w.top[lane] = 0ull;
   if (lane == 0) w.ntop = 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (tid == 0) *bbound = 0u;
+  __syncthreads();
   const int s1 = min((seg + 1) * spb, n_sub);
   for (int s = seg * spb + wave; s < s1; s += 4) {
     const int lo = s * WS, hi = min(lo + WS, V);
     if (DT == DFLASH_BF16)
-      wave_fold_bf16(reinterpret_cast<const uint16_t*>(U) + (size_t)row * V, lo, hi, K, w, lane);
+      wave_fold_bf16(reinterpret_cast<const uint16_t*>(U) + (size_t)row * V, lo, hi, K, w, lane, bbound);
     else
-      wave_fold_f32(reinterpret_cast<const uint32_t*>(U) + (size_t)row * V, lo, hi, K, w, lane);
+      wave_fold_f32(reinterpret_cast<const uint32_t*>(U) + (size_t)row * V, lo, hi, K, w, lane, bbound);
   }
   if (tid < 16) block_top[tid] = 0ull;
   __syncthreads();
