@@ -213,8 +213,11 @@ def main():
             read_gbps = nbytes / (sum(a.elapsed_time(b) for a, b in evs) * 1e-3) / 1e9
             _log(f"[bench] read ceiling {read_gbps:.1f} GB/s")
 
-    # the streaming launch reads every drafter and target logit once
-    algo = {"cycle_stream": ub + zb}
+    # the streaming launch reads every drafter and target logit once, and
+    # the gate's inputs h [B, L, hidden] and W_g [r, hidden] once
+    ps = 2 if base["param_kind"] == "bf16" else 4
+    gate_bytes = (base["B"] * base["L"] + base["r"]) * base["hidden"] * ps
+    algo = {"cycle_stream": ub + zb + gate_bytes}
     dom = max(algo, key=lambda k: kern.get(k, {}).get("avg_us", 0.0))
     achieved = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9 if dom in kern else None
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,

@@ -26,6 +26,10 @@ COMMON_FLAGS = [
     # packed fp32 arithmetic stays off: the compiler must not form
     # v_pk_{add,mul,fma}_f32 from scalar float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: in the AGPR form the streaming
+    # kernel's gate blocks added AGPRs on top of its VGPRs, and the total
+    # sets every block's occupancy
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -1,10 +1,10 @@
 // dflash_cycle: the whole draft -> select -> verify cycle in three launches
 // on the caller's stream.
 //   1. stream_kernel: one grid streams every logit once.  Its first blocks
-//      compute the gate tiles (they depend only on h and W_g), the next ones
-//      fold the drafter rows into sorted top lists (S1), the last ones reduce
-//      the target rows to chunk statistics (S5).  Nothing in the launch waits
-//      on anything else in it.
+//      fold the drafter rows into sorted top lists (S1), the next ones
+//      reduce the target rows to chunk statistics (S5), the last ones
+//      compute the gate's hidden-slice partials (S2; they depend only on h
+//      and W_g).  Nothing in the launch waits on anything else in it.
 //   2. cand_scores_kernel: one block per edge (b, t) merges the top lists of
 //      rows t-1 and t, writes row t's candidates (and their target logits),
 //      and computes the edge's pair scores (S2, S3).
@@ -28,31 +28,20 @@ union StreamLds {
 };
 
 template <int DT, int PT>
-__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U, const void* __restrict__ Z,
-                                                     const void* __restrict__ h, const void* __restrict__ W, int R,
-                                                     int H, int r, float* __restrict__ gpart, int n_gate, int gate_cols,
-                                                     int n_ks,
+__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U, const void* __restrict__ Z, int R,
                                                      int V, int K, int L, int n_sub, int spb, int n_seg,
                                                      uint64_t* __restrict__ partial, int n_chunk, int n_grp,
-                                                     const float* __restrict__ T, ChunkStat* __restrict__ stats) {
+                                                     const float* __restrict__ T, ChunkStat* __restrict__ stats,
+                                                     const void* __restrict__ h, const void* __restrict__ W, int H,
+                                                     int r, float* __restrict__ gpart, int gate_cols, int n_ks) {
   __shared__ StreamLds sh;
-  int id = blockIdx.x;
-  if (id < n_gate) {
-    if (PT == DFLASH_BF16) {
-      // id -> (row tile, column tile, hidden slice), slice fastest
-      const int ks = id % n_ks, tile = id / n_ks;
-      gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
-                        tile / gate_cols, tile - (tile / gate_cols) * gate_cols, ks, sh.red);
-    } else {
-      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, gpart, id);
-    }
-    return;
-  }
   // top-K blocks in drafter-row order, then statistics blocks in target-row
   // order: the whole grid sweeps U and then Z front to back (measured ~10%
   // faster than interleaving the two kinds, which splits the reads between
-  // two distant regions)
-  id -= n_gate;
+  // two distant regions).  The gate blocks come last and run in the
+  // launch's tail, where the sweep no longer fills the machine (in front
+  // they held slots while the sweep started: measured ~3 us slower).
+  int id = blockIdx.x;
   const int n_topk = R * n_seg;
   if (id < n_topk) {
     const int row = id / n_seg, seg = id - row * n_seg;
@@ -61,6 +50,19 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U,
     return;
   }
   id -= n_topk;
+  const int n_stat = (R / L) * (L + 1) * n_grp;
+  if (id >= n_stat) {
+    const int gi = id - n_stat;
+    if (PT == DFLASH_BF16) {
+      // gate block gi -> (row tile, column tile, hidden slice), slice fastest
+      const int ks = gi % n_ks, tile = gi / n_ks;
+      gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
+                        tile / gate_cols, tile - (tile / gate_cols) * gate_cols, ks, sh.red);
+    } else {
+      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, gpart, gi);
+    }
+    return;
+  }
   const int rowid = id / n_grp;
   const int c = (id - rowid * n_grp) * 4 + (threadIdx.x >> 6);
   if (c >= n_chunk) return;
@@ -136,18 +138,18 @@ __global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
 hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
                                const void* W_g, const float* T, char* ws, hipStream_t st) {
   const int R = d.B * d.L;
-  const int gate_cols = (d.r + 63) / 64;
+  const int n_grp = (w.n_chunk + 3) / 4;
+  const int gate_cols = (d.r + kGateCols - 1) / kGateCols;
   const int n_ks = gate_slices(d);
   const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols * n_ks : R;
-  const int n_grp = (w.n_chunk + 3) / 4;
-  const long long blocks = (long long)n_gate + (long long)R * w.n_seg + (long long)d.B * (d.L + 1) * n_grp;
-  float* g = reinterpret_cast<float*>(ws + w.gate);
+  const long long blocks = (long long)R * w.n_seg + (long long)d.B * (d.L + 1) * n_grp + n_gate;
   uint64_t* partial = reinterpret_cast<uint64_t*>(ws + w.topk_partial);
   ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws + w.stats);
+  float* gpart = reinterpret_cast<float*>(ws + w.gate);
 #define DF_STREAM(DT, PT)                                                                                     \
-  hipLaunchKernelGGL((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), 0, st, U, Z, h, W_g, R,      \
-                     d.hidden, d.r, g, n_gate, gate_cols, n_ks, d.V, d.K, d.L, w.n_sub, w.spb, w.n_seg,        \
-                     partial, w.n_chunk, n_grp, T, stats)
+  hipLaunchKernelGGL((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), 0, st, U, Z, R, d.V, d.K,   \
+                     d.L, w.n_sub, w.spb, w.n_seg, partial, w.n_chunk, n_grp, T, stats, h, W_g, d.hidden, d.r, \
+                     gpart, gate_cols, n_ks)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_STREAM(DFLASH_BF16, DFLASH_BF16); else DF_STREAM(DFLASH_BF16, DFLASH_F32);
   } else {

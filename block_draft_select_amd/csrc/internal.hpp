@@ -70,8 +70,8 @@ hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* 
                            const float* T, const uint64_t* seed, uint64_t cycle,
                            const ChunkStat* stats, int32_t* accept_len, int32_t* out_tok,
                            hipStream_t st);
-// dflash_cycle: (1) gate + top-K lists + chunk statistics, (2) candidates
-// + pair scores, (3) trace + verify
+// dflash_cycle: (1) top-K lists + chunk statistics + gate slices,
+// (2) candidates + pair scores, (3) trace + verify
 hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
                                const void* W_g, const float* T, char* ws, hipStream_t st);
 hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) void trace_kernel(const float* __restrict__ S, 
 hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* gpart, hipStream_t st) {
   const int R = d.B * d.L;
   if (d.param_dtype == DFLASH_BF16) {
-    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + 63) / 64), (unsigned)gate_slices(d));
+    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols), (unsigned)gate_slices(d));
     hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(h),
                        reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, gpart);
   } else {

@@ -17,70 +17,73 @@ typedef float v4f32 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- gate
 
 constexpr int kGateWaves = 4;          // waves per gate block
-constexpr int kGateRed = kGateWaves * 4 * 4 * 64;  // floats of LDS per gate block
+constexpr int kGateCT = 2;             // 16-column tiles per gate block (32 columns)
+constexpr int kGateCols = 16 * kGateCT;
+constexpr int kGateRed = kGateWaves * kGateCT * 4 * 64;  // floats of LDS per gate block
 
-// Partial pre-activation of one 16-row x 64-column tile of W_g h over
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Partial pre-activation of one 16-row x 32-column tile of W_g h over
 // hidden slice ks ([ks * 256, ks * 256 + 256) of the hidden dimension):
-// part[ks][row][col] = sum over the slice of h[row][k] W_g[col][k].  The
-// slice's k-steps of 16 go to the waves round robin (at most four each) and
-// every operand load is issued before the first MFMA, so a block waits on
-// memory once; the four waves' tiles are summed through `red` (LDS) in wave
-// order.  MFMA 16x16x16 bf16 operand layout: lane l holds
-// A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16]; the
-// accumulator holds D[4 (l / 16) + i][l % 16].  A = h and B[k][n] =
-// W_g[n][k], both contiguous along k: one 8-byte load each.
+// part[ks][row][col] = sum over the slice of h[row][k] W_g[col][k].  Wave w
+// takes the contiguous quarter [64 w, 64 w + 64) of the slice as two
+// v_mfma_f32_16x16x32_bf16 steps per 16-column tile; every operand load is
+// issued before the first MFMA, so a block waits on memory once, and each
+// wave reads 128 contiguous bytes of every row it touches.  The four
+// waves' tiles are summed through `red` (LDS) in wave order.  Operand
+// layout: lane l holds A[l % 16][8 (l / 16) + 0..7] and
+// B[8 (l / 16) + 0..7][l % 16] (one 16-byte load each, A = h and
+// B[k][n] = W_g[n][k], both contiguous along k); the accumulator holds
+// D[4 (l / 16) + i][l % 16].  A hidden slice shorter than 256 (hidden is a
+// multiple of 16) zero-fills the 8-element groups past its end.
 __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                   int R, int H, int r, float* __restrict__ part, int tile_row,
                                                   int tile_col, int ks, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = tile_row * 16, col0 = tile_col * 64;
-  const int k0 = ks * kGateSlice;
-  const int n_steps = min(kGateSlice, H - k0) / 16;
+  const int row0 = tile_row * 16, col0 = tile_col * kGateCols;
+  const int kend = min(H, ks * kGateSlice + kGateSlice);
+  const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;  // this lane's first k
   const int arow = row0 + (lane & 15);
-  const int kq = k0 + (lane >> 4) * 4;
-  const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kq;
-  const uint16_t* wp[4];
-  bool wok[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int col = col0 + ct * 16 + (lane & 15);
-    wok[ct] = col < r;
-    wp[ct] = W + (size_t)min(col, r - 1) * H + kq;
-  }
-  constexpr int kSteps = kGateSlice / 16 / kGateWaves;
-  v4i16 a[kSteps], bv[kSteps][4];
+  const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
+  const int col = col0 + (lane & 15);
+  const uint16_t* wp = W + kw;
+  constexpr int kSteps = kGateSlice / kGateWaves / 32;  // 32-wide k-steps per wave
+  const bf16x8 zero = {};
+  bf16x8 a[kSteps], bv[kSteps][kGateCT];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
-    const int s = wave + kGateWaves * i;
-    const bool ok = s < n_steps;
-    a[i] = ok && arow < R ? *reinterpret_cast<const v4i16*>(hp + s * 16) : (v4i16){0, 0, 0, 0};
+    const bool ok = kw + 32 * i < kend;
+    a[i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      bv[i][ct] = ok && wok[ct] ? *reinterpret_cast<const v4i16*>(wp[ct] + s * 16) : (v4i16){0, 0, 0, 0};
+    for (int ct = 0; ct < kGateCT; ++ct) {
+      const int c = col + ct * 16;
+      bv[i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
+    }
   }
-  v4f32 acc[4];
+  v4f32 acc[kGateCT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < kGateCT; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kSteps; ++i)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], bv[i][ct], acc[ct], 0, 0, 0);
+    for (int ct = 0; ct < kGateCT; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[i][ct], acc[ct], 0, 0, 0);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < kGateCT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wave * 4 + ct) * 4 + i) * kWave + lane] = acc[ct][i];
+    for (int i = 0; i < 4; ++i) red[((wave * kGateCT + ct) * 4 + i) * kWave + lane] = acc[ct][i];
   __syncthreads();
   float* out = part + (size_t)ks * R * r;
 #pragma unroll
-  for (int o4 = 0; o4 < 4; ++o4) {
-    const int o = tid + o4 * 256;
+  for (int o2 = 0; o2 < kGateCT; ++o2) {
+    const int o = tid + o2 * 256;
     const int ct = o >> 8, i = (o >> 6) & 3, ln = o & 63;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGateWaves; ++w) v += red[((w * 4 + ct) * 4 + i) * kWave + ln];
+    for (int w = 0; w < kGateWaves; ++w) v += red[((w * kGateCT + ct) * 4 + i) * kWave + ln];
     const int row = row0 + (ln >> 4) * 4 + i;
-    const int col = col0 + ct * 16 + (ln & 15);
-    if (row < R && col < r) out[(size_t)row * r + col] = v;
+    const int c = col0 + ct * 16 + (ln & 15);
+    if (row < R && c < r) out[(size_t)row * r + c] = v;
   }
 }
 
