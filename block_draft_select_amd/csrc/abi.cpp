@@ -92,7 +92,10 @@ Profiler& prof() {
   return *p;
 }
 
-// launch `f` on `st`, bracketed by events when the timer is on
+// Run `f` (which enqueues on `st`), timed when the timer is on.  Entry
+// points of a single launch hand the events to that launch, which records
+// them at the kernel's own start and end; the two-launch top-K entry point
+// brackets its launches with events on the stream.
 template <class F>
 hipError_t timed(int kernel, hipStream_t st, F f) {
   Profiler& P = prof();
@@ -104,12 +107,27 @@ hipError_t timed(int kernel, hipStream_t st, F f) {
       b = P.take();
     }
   }
-  if (a) hipEventRecord(a, st);
-  const hipError_t e = f();
+  const bool on_stream = kernel == DFLASH_KERNEL_TOPK;
   if (a && b) {
-    hipEventRecord(b, st);
+    if (on_stream) {
+      hipEventRecord(a, st);
+    } else {
+      dfk::g_launch_start = a;
+      dfk::g_launch_stop = b;
+    }
+  }
+  const hipError_t e = f();
+  const bool launched = !(dfk::g_launch_start || dfk::g_launch_stop);
+  dfk::g_launch_start = dfk::g_launch_stop = nullptr;
+  if (a && b) {
+    if (on_stream) hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(P.mu);
-    P.pending[kernel].push_back({a, b});
+    if (e == hipSuccess && launched) {
+      P.pending[kernel].push_back({a, b});
+    } else {
+      P.pool.push_back(a);
+      P.pool.push_back(b);
+    }
   }
   return e;
 }
@@ -122,6 +140,8 @@ dflash_status hip_status(hipError_t e, const char* what) {
 }  // namespace
 
 namespace dfk {
+
+thread_local hipEvent_t g_launch_start = nullptr, g_launch_stop = nullptr;
 
 // Sub-segments per top-K block: by default the smallest multiple of 4 that
 // keeps the top-K part of the grid at or below 2048 blocks; at least enough

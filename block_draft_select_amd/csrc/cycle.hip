@@ -147,7 +147,7 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
   ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws + w.stats);
   float* gpart = reinterpret_cast<float*>(ws + w.gate);
 #define DF_STREAM(DT, PT)                                                                                     \
-  hipLaunchKernelGGL((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), 0, st, U, Z, R, d.V, d.K,   \
+  launch((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), st, U, Z, R, d.V, d.K,   \
                      d.L, w.n_sub, w.spb, w.n_seg, partial, w.n_chunk, n_grp, T, stats, h, W_g, d.hidden, d.r, \
                      gpart, gate_cols, n_ks)
   if (d.logit_dtype == DFLASH_BF16) {
@@ -167,7 +167,7 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
   const float* g = reinterpret_cast<const float*>(ws + w.gate);
   float* zc = reinterpret_cast<float*>(ws + w.zc);
 #define DF_SCORES(DT, PT)                                                                                      \
-  hipLaunchKernelGGL((cand_scores_kernel<DT, PT>), grid, dim3(256), 0, st, partial, w.n_seg, x0, E, g,         \
+  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g,         \
                      gate_slices(d), Z, d.L, d.V, d.K, d.r, cand_idx, cand_logit, zc, S)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);
@@ -186,11 +186,11 @@ hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const 
   const float* zc = reinterpret_cast<const float*>(ws + w.zc);
   const ChunkStat* stats = reinterpret_cast<const ChunkStat*>(ws + w.stats);
   if (d.logit_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(trace_finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K,
+    launch(trace_finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K,
                        w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
                        out_tok);
   else
-    hipLaunchKernelGGL(trace_finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K,
+    launch(trace_finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K,
                        w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
                        out_tok);
   return hipGetLastError();

@@ -2,6 +2,7 @@
 // geometry constants, the workspace layout and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -51,6 +52,18 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const dflash_dims& d);
+
+// Events the next kernel launch on this thread records at the kernel's own
+// start and end (hipExtLaunchKernel: the dispatch's timestamps, not the
+// stream's), set by the per-kernel timer and consumed by that launch.
+extern thread_local hipEvent_t g_launch_start, g_launch_stop;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  hipEvent_t a = g_launch_start, b = g_launch_stop;
+  g_launch_start = g_launch_stop = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+}
 
 // ---- launchers (each enqueues on `st`; returns the launch status) ----
 

@@ -49,21 +49,21 @@ unsigned grid_for(size_t n16) {
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   const size_t n16 = bytes / 16;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n16,
+  launch(fill_zero_kernel, dim3(grid_for(n16)), dim3(256), st, reinterpret_cast<uint4*>(p), n16,
                      reinterpret_cast<uint8_t*>(p) + n16 * 16, bytes - n16 * 16);
   return hipGetLastError();
 }
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
   const size_t n16 = bytes / 16;
-  hipLaunchKernelGGL(read_probe_kernel, dim3(grid_for(n16)), dim3(256), 0, st,
+  launch(read_probe_kernel, dim3(grid_for(n16)), dim3(256), st,
                      reinterpret_cast<const uint4*>(buf), n16, sink);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st) {
   const size_t n16 = bytes / 16;
-  hipLaunchKernelGGL(copy_probe_kernel, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(dst),
+  launch(copy_probe_kernel, dim3(grid_for(n16)), dim3(256), st, reinterpret_cast<uint4*>(dst),
                      reinterpret_cast<const uint4*>(src), n16);
   return hipGetLastError();
 }

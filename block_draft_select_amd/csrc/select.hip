@@ -94,10 +94,10 @@ hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, flo
   const int R = d.B * d.L;
   if (d.param_dtype == DFLASH_BF16) {
     const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols), (unsigned)gate_slices(d));
-    hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(h),
+    launch(gate_mfma_kernel, grid, dim3(256), st, reinterpret_cast<const uint16_t*>(h),
                        reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, gpart);
   } else {
-    hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)R), dim3(256), 0, st, reinterpret_cast<const float*>(h),
+    launch(gate_f32_kernel, dim3((unsigned)R), dim3(256), st, reinterpret_cast<const float*>(h),
                        reinterpret_cast<const float*>(W_g), d.hidden, d.r, gpart);
   }
   return hipGetLastError();
@@ -109,10 +109,10 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
   const dim3 grid((unsigned)(d.B * d.L));
   const int n_ks = gate_slices(d);
   if (d.param_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(scores_kernel<DFLASH_BF16>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, gpart,
+    launch(scores_kernel<DFLASH_BF16>, grid, dim3(256), st, x0, cand_idx, cand_logit, E, gpart,
                        n_ks, d.L, d.V, d.K, d.r, S);
   else
-    hipLaunchKernelGGL(scores_kernel<DFLASH_F32>, grid, dim3(256), 0, st, x0, cand_idx, cand_logit, E, gpart,
+    launch(scores_kernel<DFLASH_F32>, grid, dim3(256), st, x0, cand_idx, cand_logit, E, gpart,
                        n_ks, d.L, d.V, d.K, d.r, S);
   return hipGetLastError();
 }
@@ -120,7 +120,7 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
                         const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
                         float* q, hipStream_t st) {
-  hipLaunchKernelGGL(trace_kernel, dim3((unsigned)d.B), dim3(64), 0, st, S, cand_idx, T, seed, cycle, d.L,
+  launch(trace_kernel, dim3((unsigned)d.B), dim3(64), st, S, cand_idx, T, seed, cycle, d.L,
                      d.V, d.K, path_rank, draft_tok, q);
   return hipGetLastError();
 }

@@ -44,14 +44,14 @@ hipError_t launch_topk(const dflash_dims& d, const WsLayout& w, const void* U, i
   uint64_t* partial = reinterpret_cast<uint64_t*>(ws + w.topk_partial);
   const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
   if (d.logit_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(topk_partial_kernel<DFLASH_BF16>, grid, dim3(kTopkThreads), 0, st, U, d.V, d.K, w.n_sub,
+    launch(topk_partial_kernel<DFLASH_BF16>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub,
                        w.spb, partial);
   else
-    hipLaunchKernelGGL(topk_partial_kernel<DFLASH_F32>, grid, dim3(kTopkThreads), 0, st, U, d.V, d.K, w.n_sub,
+    launch(topk_partial_kernel<DFLASH_F32>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub,
                        w.spb, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_output_kernel, dim3((unsigned)rows), dim3(256), 0, st, partial, d.K, w.n_seg, cand_idx,
+  launch(topk_output_kernel, dim3((unsigned)rows), dim3(256), st, partial, d.K, w.n_seg, cand_idx,
                      cand_logit);
   return hipGetLastError();
 }

@@ -40,9 +40,9 @@ hipError_t launch_stats(const dflash_dims& d, const WsLayout& w, const void* Z, 
                         hipStream_t st) {
   const dim3 grid((unsigned)((w.n_chunk + 3) / 4), (unsigned)(d.B * (d.L + 1)));
   if (d.logit_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(stats_kernel<DFLASH_BF16>, grid, dim3(256), 0, st, Z, d.L, d.V, w.n_chunk, T, stats);
+    launch(stats_kernel<DFLASH_BF16>, grid, dim3(256), st, Z, d.L, d.V, w.n_chunk, T, stats);
   else
-    hipLaunchKernelGGL(stats_kernel<DFLASH_F32>, grid, dim3(256), 0, st, Z, d.L, d.V, w.n_chunk, T, stats);
+    launch(stats_kernel<DFLASH_F32>, grid, dim3(256), st, Z, d.L, d.V, w.n_chunk, T, stats);
   return hipGetLastError();
 }
 
@@ -53,10 +53,10 @@ hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* 
                            hipStream_t st) {
   const dim3 grid((unsigned)d.B);
   if (d.logit_dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K, w.n_chunk, T,
+    launch(finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K, w.n_chunk, T,
                        seed, cycle, cand_idx, path_rank, q, stats, accept_len, out_tok);
   else
-    hipLaunchKernelGGL(finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), 0, st, Z, d.L, d.V, d.K, w.n_chunk, T,
+    launch(finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K, w.n_chunk, T,
                        seed, cycle, cand_idx, path_rank, q, stats, accept_len, out_tok);
   return hipGetLastError();
 }
