@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
   const int b = bt / L, t = bt - b * L;
   const int tid = threadIdx.x;
   if (tid < 16) cl.prev[tid] = cl.cur[tid] = 0ull;
+  edge_gate(cl.e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
   merge_two_rows(partial + (size_t)(t > 0 ? bt - 1 : bt) * n_seg * 16, t > 0, partial + (size_t)bt * n_seg * 16,
                  n_seg, K, cl.keys, cl.prev, cl.cur);
   if (tid < 16) {
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
     zv = DT == DFLASH_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
                            : reinterpret_cast<const float*>(Z)[zi];
   }
-  edge_scores<PT>(cl.e, E, gpart, n_ks, (size_t)gridDim.x * r, bt, K, r, S + (size_t)bt * K * K);
+  edge_contract<PT>(cl.e, E, K, r, S + (size_t)bt * K * K);
   if (tid < K) zc[(size_t)bt * K + tid] = zv;
 }
 

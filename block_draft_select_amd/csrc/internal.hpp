@@ -85,6 +85,7 @@ hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* 
                            hipStream_t st);
 // dflash_cycle: (1) top-K lists + chunk statistics + gate slices,
 // (2) candidates + pair scores, (3) trace + verify
+hipError_t launch_topk_lists(const dflash_dims& d, const WsLayout& w, const void* U, char* ws, hipStream_t st);
 hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
                                const void* W_g, const float* T, char* ws, hipStream_t st);
 hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,

@@ -46,8 +46,9 @@ __global__ __launch_bounds__(256) void scores_kernel(const int32_t* __restrict__
     e.cidx[tid] = c;
     e.cl[tid] = cl;
   }
+  edge_gate(e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
   __syncthreads();
-  edge_scores<PT>(e, E, gpart, n_ks, (size_t)gridDim.x * r, bt, K, r, S + (size_t)bt * K * K);
+  edge_contract<PT>(e, E, K, r, S + (size_t)bt * K * K);
 }
 
 // one wave per stream

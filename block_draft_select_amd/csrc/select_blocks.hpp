@@ -106,105 +106,121 @@ __device__ __forceinline__ float gate_value(const float* __restrict__ part, int 
                                             int col) {
   const float* p = part + (size_t)row * r + col;
   float z = 0.f;
-  for (int ks = 0; ks < n_ks; ++ks) z += p[ks * stride];
+  for (int k0 = 0; k0 < n_ks; k0 += 8) {  // eight slices' loads in flight at once
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = k0 + i < n_ks ? p[(k0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i < n_ks) z += v[i];
+  }
   return 1.0f / (1.0f + expf(-z));
 }
 
 // ---------------------------------------------------------------- edge scores
 
-constexpr int kRowPad = DFLASH_R_MAX + 4;  // 16-byte aligned LDS rows
-
+// LDS of one edge's scores in a 256-thread block (small enough to share a
+// launch with the streaming blocks without costing them occupancy)
 struct EdgeLds {
-  float A[16][kRowPad];  // predecessor rows scaled by g_t
-  float C[16][kRowPad];  // candidate rows
-  float red[4][4][kWave];  // per-wave partial 16 x 16 products (MFMA accumulator layout)
   float g[DFLASH_R_MAX];   // gate of this edge
-  int pidx[16], cidx[16];
-  float cl[16];
+  float red[4][4][kWave];  // per-wave partial 16 x 16 products (MFMA accumulator layout)
+  int pidx[16], cidx[16];  // predecessor / candidate tokens (-1: zero row)
+  float cl[16];            // candidate drafter logits U_t(b)
 };
 
-// 16 embedding rows E[idx[i]] (zero rows where idx[i] < 0) of width r, one
-// 256-thread block's share per thread: loaded into registers first, stored
-// to LDS (fp32) afterwards, so that several row sets can be in flight.
-template <int PT>
-struct RowLoad {
-  static constexpr int EPU = PT == DFLASH_BF16 ? 8 : 4;  // values per 16-byte load
-  static constexpr int NU = PT == DFLASH_BF16 ? 2 : 4;   // loads per thread (16 rows x 256 values max)
-  uint4 v[NU];
-
-  __device__ __forceinline__ void load(const void* __restrict__ E, const int* idx, int r) {
-    const int tid = threadIdx.x;
-    const int upr = r / EPU;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = tid + k * 256;
-      const int row = u / upr, col = (u - row * upr) * EPU;
-      v[k] = make_uint4(0, 0, 0, 0);
-      if (row < 16 && idx[row] >= 0) {
-        if (PT == DFLASH_BF16)
-          v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(E) + (size_t)idx[row] * r + col);
-        else
-          v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(E) + (size_t)idx[row] * r + col);
-      }
-    }
-  }
-
-  // dst[row][col] = value, multiplied by g[col] when g is given
-  __device__ __forceinline__ void store(int r, const float* g, float (*dst)[kRowPad]) const {
-    const int tid = threadIdx.x;
-    const int upr = r / EPU;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = tid + k * 256;
-      const int row = u / upr, col = (u - row * upr) * EPU;
-      if (row < 16) {
-        float f[EPU];
-        if (PT == DFLASH_BF16) {
-          f[0] = bf16_lo(v[k].x); f[1] = bf16_hi(v[k].x);
-          f[2] = bf16_lo(v[k].y); f[3] = bf16_hi(v[k].y);
-          f[4] = bf16_lo(v[k].z); f[5] = bf16_hi(v[k].z);
-          f[6] = bf16_lo(v[k].w); f[7] = bf16_hi(v[k].w);
-        } else {
-          f[0] = __uint_as_float(v[k].x); f[1] = __uint_as_float(v[k].y);
-          f[2] = __uint_as_float(v[k].z); f[3] = __uint_as_float(v[k].w);
-        }
-#pragma unroll
-        for (int e = 0; e < EPU; ++e) dst[row][col + e] = g ? f[e] * g[col + e] : f[e];
-      }
-    }
-  }
-};
-
-// Scores of edge (b, t) (drafter row `row`) from the staged index lists in
-// `e` (pidx, cidx, cl filled, barrier passed):
-// S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k], with g_t summed
-// from the gate slices (gpart, n_ks slices `gstride` apart).
-// The 16 x r x 16 contraction runs on the matrix cores in fp32
-// (v_mfma_f32_16x16x4_f32): wave w takes the k-range [w r/4, (w+1) r/4),
-// A = g-scaled predecessor rows, B[k][j] = candidate row j; lane l feeds
-// A[l % 16][k0 + l / 16] and B[k0 + l / 16][l % 16] (with the LDS row pitch
-// of 260 floats the 64 lanes hit 64 distinct banks) and holds
-// D[4 (l / 16) + v][l % 16].  The four partial products are summed in wave
-// order.
-template <int PT>
-__device__ __forceinline__ void edge_scores(EdgeLds& e, const void* __restrict__ E, const float* __restrict__ gpart,
-                                            int n_ks, size_t gstride, int row, int K, int r,
-                                            float* __restrict__ S_edge) {
-  RowLoad<PT> a, c;
-  a.load(E, e.pidx, r);
-  c.load(E, e.cidx, r);
+// g_t[k] for every k < r of drafter row `row` into e.g (threads k < r)
+__device__ __forceinline__ void edge_gate(EdgeLds& e, const float* __restrict__ gpart, int n_ks, size_t gstride,
+                                          int row, int r) {
   if ((int)threadIdx.x < r) e.g[threadIdx.x] = gate_value(gpart, n_ks, gstride, row, r, threadIdx.x);
-  __syncthreads();
-  a.store(r, e.g, e.A);
-  c.store(r, nullptr, e.C);
-  __syncthreads();
+}
+
+// The n = r / 16 consecutive stored values E[idx][k0 .. k0 + n) (n <= 16;
+// zeros when idx < 0), raw: 16-byte loads when the run allows them (the
+// run then starts 16-byte aligned), single values otherwise.
+template <int PT>
+struct Run {
+  static constexpr int NU = PT == DFLASH_BF16 ? 2 : 4;  // 16-byte units of 16 values
+  uint4 u[NU];
+
+  __device__ __forceinline__ void load(const void* __restrict__ E, int idx, int r, int k0, int n) {
+#pragma unroll
+    for (int h = 0; h < NU; ++h) u[h] = make_uint4(0, 0, 0, 0);
+    if (idx < 0) return;
+    constexpr int EPU = 16 / NU;  // values per unit
+    if (PT == DFLASH_BF16) {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(E) + (size_t)idx * r + k0;
+      if (n % EPU == 0) {
+#pragma unroll
+        for (int h = 0; h < NU; ++h)
+          if (EPU * h < n) u[h] = reinterpret_cast<const uint4*>(p)[h];
+      } else {
+        uint32_t w[8] = {};
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if (s < n) w[s >> 1] |= (uint32_t)p[s] << (16 * (s & 1));
+#pragma unroll
+        for (int h = 0; h < NU; ++h) u[h] = make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+      }
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(E) + (size_t)idx * r + k0;
+      if (n % EPU == 0) {
+#pragma unroll
+        for (int h = 0; h < NU; ++h)
+          if (EPU * h < n) u[h] = reinterpret_cast<const uint4*>(p)[h];
+      } else {
+        uint32_t w[16] = {};
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if (s < n) w[s] = p[s];
+#pragma unroll
+        for (int h = 0; h < NU; ++h) u[h] = make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+      }
+    }
+  }
+
+  // value s of the run as fp32 (s a compile-time constant after unrolling)
+  __device__ __forceinline__ float at(int s) const {
+    const uint4 q = u[PT == DFLASH_BF16 ? s >> 3 : s >> 2];
+    const int c = PT == DFLASH_BF16 ? (s >> 1) & 3 : s & 3;
+    const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+    if (PT == DFLASH_BF16) return (s & 1) ? bf16_hi(w) : bf16_lo(w);
+    return __uint_as_float(w);
+  }
+};
+
+// Scores of one edge from the staged lists in `e` (pidx, cidx, cl and g
+// filled, barrier passed):
+// S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k].
+// The 16 x r x 16 contraction runs on the matrix cores in fp32
+// (v_mfma_f32_16x16x4_f32) with operands taken straight from the gathered
+// embedding rows: wave w covers k in [w r/4, (w+1) r/4); lane group
+// q = l / 16 owns the run of n = r/16 consecutive k starting at
+// k(q) = (4 w + q) n and feeds its s-th value at step s, so lane l gives
+// A[l % 16][k(q) + s] = E[pidx_{l%16}, k] g_t[k] and B[k(q) + s][l % 16] =
+// E[cidx_{l%16}, k] (each lane reads one contiguous run per row: a wave
+// reads whole 128-byte row pieces) and holds D[4 (l / 16) + v][l % 16].
+// The four waves' products are summed in wave order.  The split entry
+// point and the fused cycle both call this, so their scores are identical.
+template <int PT>
+__device__ __forceinline__ void edge_contract(EdgeLds& e, const void* __restrict__ E, int K, int r,
+                                              float* __restrict__ S_edge) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int steps = r >> 4;  // k-steps of 4 per wave
-  const int ka = wave * (r >> 2) + (lane >> 4);
-  const float* ar = &e.A[lane & 15][ka];
-  const float* cr = &e.C[lane & 15][ka];
+  const int n = r >> 4;
+  const int k0 = ((wave << 2) + (lane >> 4)) * n;
+  Run<PT> av, cv;
+  av.load(E, e.pidx[lane & 15], r, k0, n);
+  cv.load(E, e.cidx[lane & 15], r, k0, n);
   v4f32 acc = (v4f32){0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < steps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[4 * s], cr[4 * s], acc, 0, 0, 0);
+  if (n == 16) {  // r = 256: straight-line steps
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.at(s) * e.g[k0 + s], cv.at(s), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < n) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.at(s) * e.g[k0 + s], cv.at(s), acc, 0, 0, 0);
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) e.red[wave][v][lane] = acc[v];
   __syncthreads();

@@ -38,21 +38,23 @@ __global__ __launch_bounds__(256) void topk_output_kernel(const uint64_t* __rest
 
 }  // namespace
 
-hipError_t launch_topk(const dflash_dims& d, const WsLayout& w, const void* U, int32_t* cand_idx,
-                       float* cand_logit, char* ws, hipStream_t st) {
+hipError_t launch_topk_lists(const dflash_dims& d, const WsLayout& w, const void* U, char* ws, hipStream_t st) {
   const int rows = d.B * d.L;
   uint64_t* partial = reinterpret_cast<uint64_t*>(ws + w.topk_partial);
   const dim3 grid((unsigned)w.n_seg, (unsigned)rows);
   if (d.logit_dtype == DFLASH_BF16)
-    launch(topk_partial_kernel<DFLASH_BF16>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub,
-                       w.spb, partial);
+    launch(topk_partial_kernel<DFLASH_BF16>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub, w.spb, partial);
   else
-    launch(topk_partial_kernel<DFLASH_F32>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub,
-                       w.spb, partial);
-  hipError_t e = hipGetLastError();
+    launch(topk_partial_kernel<DFLASH_F32>, grid, dim3(kTopkThreads), st, U, d.V, d.K, w.n_sub, w.spb, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const dflash_dims& d, const WsLayout& w, const void* U, int32_t* cand_idx,
+                       float* cand_logit, char* ws, hipStream_t st) {
+  hipError_t e = launch_topk_lists(d, w, U, ws, st);
   if (e != hipSuccess) return e;
-  launch(topk_output_kernel, dim3((unsigned)rows), dim3(256), st, partial, d.K, w.n_seg, cand_idx,
-                     cand_logit);
+  launch(topk_output_kernel, dim3((unsigned)(d.B * d.L)), dim3(256), st,
+         reinterpret_cast<const uint64_t*>(ws + w.topk_partial), d.K, w.n_seg, cand_idx, cand_logit);
   return hipGetLastError();
 }
 

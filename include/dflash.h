@@ -27,10 +27,9 @@
  *     dense row-major with the shapes given in brackets.  U, Z, E, W_g and h
  *     must be 16-byte aligned.
  *   - Scratch lives in a caller-provided device workspace of at least
- *     dflash_workspace_bytes() bytes, zero-filled before its first use
- *     (dflash_workspace_init does that).  The library leaves its counters
- *     at zero after every completed call, so the same workspace can be
- *     reused by later calls on the same stream without clearing it again.
+ *     dflash_workspace_bytes() bytes; its contents need no initialisation
+ *     (dflash_workspace_init zero-fills one for callers who want defined
+ *     contents).
  *     Calls that overlap in time must not share a workspace.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream).  Outputs are valid once the caller
@@ -169,10 +168,11 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
                             int32_t* out_tok, void* ws, size_t ws_bytes, void* stream);
 
 /* One whole cycle: dflash_topk, dflash_pair_scores, dflash_trace and
- * dflash_verify on one stream, with identical results, in three launches.  The intermediate
- * outputs (cand_idx [B,L,K], cand_logit [B,L,K], S [B,L,K,K],
- * path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written where the
- * caller passes non-NULL pointers and kept in the workspace otherwise. */
+ * dflash_verify on one stream, with identical results, in three launches.
+ * The intermediate outputs (cand_idx [B,L,K], cand_logit [B,L,K],
+ * S [B,L,K,K], path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written
+ * where the caller passes non-NULL pointers and kept in the workspace
+ * otherwise. */
 dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
                            const int32_t* x0, const void* E, const void* W_g, const void* h,
                            const float* T, const uint64_t* seed, uint64_t cycle,
