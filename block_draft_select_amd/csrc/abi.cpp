@@ -181,6 +181,8 @@ WsLayout ws_layout(const dflash_dims& d) {
   w.draft_tok = o;    o = align256(o + R * sizeof(int32_t));
   w.q = o;            o = align256(o + R * d.K * sizeof(float));
   w.stats = o;        o = align256(o + (size_t)d.B * (d.L + 1) * w.n_chunk * sizeof(ChunkStat));
+  w.jstar = o;        o = align256(o + R * d.K * sizeof(int32_t));
+  w.qtab = o;         o = align256(o + R * d.K * d.K * sizeof(float));
   w.total = o;
   return w;
 }
@@ -332,10 +334,10 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, c
           return dfk::launch_cycle_stream(*d, w, U, Z, h, W_g, T, base, st);
         }), "stream launch")) return s;
     if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
-          return dfk::launch_cycle_scores(*d, w, x0, E, Z, base, cand_idx, cand_logit, S, st);
+          return dfk::launch_cycle_scores(*d, w, x0, E, Z, T, seed, cycle, base, cand_idx, cand_logit, S, st);
         }), "scores launch")) return s;
     return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
-      return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, S, T, seed, cycle, base, path_rank, draft_tok, q,
+      return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, path_rank, draft_tok, q,
                                         accept_len, out_tok, st);
     }), "finalize launch");
   } catch (...) {

@@ -7,10 +7,13 @@
 //      and W_g).  Nothing in the launch waits on anything else in it.
 //   2. cand_scores_kernel: one block per edge (b, t) merges the top lists of
 //      rows t-1 and t, writes row t's candidates (and their target logits),
-//      and computes the edge's pair scores (S2, S3).
-//   3. trace_finalize_kernel: one block per stream walks the trace (S4, one
-//      wave) while the other waves combine the chunk statistics, then runs
-//      the accept tests and the residual/bonus draw (S6).
+//      computes the edge's pair scores (S2, S3), and decides the edge's K
+//      rows of the trace table: for every predecessor rank i, the walk's
+//      next rank and q (S4).
+//   3. trace_finalize_kernel: one block per stream combines the chunk
+//      statistics (one wave per target row), walks the decided table (L
+//      look-ups), then runs the accept tests and the residual/bonus draw
+//      (S6).
 #include "stats_blocks.hpp"
 #include "topk_blocks.hpp"
 
@@ -40,7 +43,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U,
   // faster than interleaving the two kinds, which splits the reads between
   // two distant regions).  The gate blocks come last and run in the
   // launch's tail, where the sweep no longer fills the machine (in front
-  // they held slots while the sweep started: measured ~3 us slower).
+  // they held slots while the sweep started: measured ~3 us slower; placed
+  // anywhere inside the statistics part, 1.3 to 2.2 us slower).
   int id = blockIdx.x;
   const int n_topk = R * n_seg;
   if (id < n_topk) {
@@ -82,17 +86,39 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
                                                           const int32_t* __restrict__ x0, const void* __restrict__ E,
                                                           const float* __restrict__ gpart, int n_ks,
                                                           const void* __restrict__ Z,
-                                                          int L, int V, int K, int r, int32_t* __restrict__ cand_idx,
+                                                          int L, int V, int K, int r, const float* __restrict__ T,
+                                                          const uint64_t* __restrict__ seed, uint64_t cycle,
+                                                          int32_t* __restrict__ cand_idx,
                                                           float* __restrict__ cand_logit, float* __restrict__ zc,
-                                                          float* __restrict__ S) {
+                                                          float* __restrict__ S, int32_t* __restrict__ jstar,
+                                                          float* __restrict__ qtab) {
   __shared__ CandLds cl;
   const int bt = blockIdx.x;
   const int b = bt / L, t = bt - b * L;
   const int tid = threadIdx.x;
   if (tid < 16) cl.prev[tid] = cl.cur[tid] = 0ull;
+  // every independent load first: the two rows' lists (registers), the
+  // gate slices, the trace inputs; the trace uniform is computed while
+  // they are in flight
+  constexpr int KPT = 2 * kTopkCycleMerge / 256;  // list keys per thread
+  const int nk = n_seg * 16;
+  const uint64_t* l0 = partial + (size_t)(t > 0 ? bt - 1 : bt) * nk;
+  const uint64_t* l1 = partial + (size_t)bt * nk;
+  uint64_t kv[KPT];
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const int i = tid + q * 256;
+    kv[q] = i < nk ? (t > 0 ? l0[i] : 0ull) : (i < 2 * nk ? l1[i - nk] : 0ull);
+  }
+  const float Tb = T[b];
+  const uint64_t sd = seed[b];
+  const uint32_t u = stream_block(sd, cycle, (uint32_t)(t + 1), 0u).x;  // the trace uniform of position t
   edge_gate(cl.e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
-  merge_two_rows(partial + (size_t)(t > 0 ? bt - 1 : bt) * n_seg * 16, t > 0, partial + (size_t)bt * n_seg * 16,
-                 n_seg, K, cl.keys, cl.prev, cl.cur);
+#pragma unroll
+  for (int q = 0; q < KPT; ++q)
+    if (tid + q * 256 < 2 * nk) cl.keys[tid + q * 256] = kv[q];
+  __syncthreads();
+  merge_two_staged(cl.keys, n_seg, K, cl.prev, cl.cur);
   if (tid < 16) {
     int p = -1, c = -1;
     float v = 0.f;
@@ -118,20 +144,29 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
     zv = DT == DFLASH_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
                            : reinterpret_cast<const float*>(Z)[zi];
   }
-  edge_contract<PT>(cl.e, E, K, r, S + (size_t)bt * K * K);
+  const float sv = edge_contract<PT>(cl.e, E, K, r, S + (size_t)bt * K * K);
   if (tid < K) zc[(size_t)bt * K + tid] = zv;
+  // S4's table rows (t, i) of this edge: the walk's decision and q from
+  // every predecessor rank i (thread tid holds S[tid / 16][tid % 16])
+  const double invT = Tb > 0.0f ? 1.0 / (double)Tb : 0.0;
+  const int i = tid >> 4, j = tid & 15;
+  float qv;
+  const int jd = trace_row_decide(sv, i < K && j < K, (tid & 63) >> 4, j, Tb, invT, u, K, qv);
+  if (i < K && j < K) qtab[((size_t)bt * K + i) * K + j] = qv;
+  if (i < K && j == 0) jstar[(size_t)bt * K + i] = jd;
 }
 
 template <int DT>
 __global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
     const void* __restrict__ Z, int L, int V, int K, int n_chunk, const float* __restrict__ T,
     const uint64_t* __restrict__ seed, uint64_t cycle, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ zc, const float* __restrict__ S, int32_t* __restrict__ path_rank,
+    const float* __restrict__ zc, const int32_t* __restrict__ jstar, const float* __restrict__ qtab,
+    int32_t* __restrict__ path_rank,
     int32_t* __restrict__ draft_tok, float* __restrict__ q, const ChunkStat* __restrict__ stats,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
   __shared__ FinLds f;
-  finalize_stream<DT, true>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank,
-                            draft_tok, q, stats, accept_len, out_tok);
+  finalize_stream<DT, true>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, jstar, qtab,
+                            path_rank, draft_tok, q, stats, accept_len, out_tok);
 }
 
 }  // namespace
@@ -161,15 +196,17 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
 }
 
 hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,
-                               const void* Z, char* ws, int32_t* cand_idx, float* cand_logit, float* S,
-                               hipStream_t st) {
+                               const void* Z, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                               int32_t* cand_idx, float* cand_logit, float* S, hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.L));
   const uint64_t* partial = reinterpret_cast<const uint64_t*>(ws + w.topk_partial);
   const float* g = reinterpret_cast<const float*>(ws + w.gate);
   float* zc = reinterpret_cast<float*>(ws + w.zc);
+  int32_t* jstar = reinterpret_cast<int32_t*>(ws + w.jstar);
+  float* qtab = reinterpret_cast<float*>(ws + w.qtab);
 #define DF_SCORES(DT, PT)                                                                                      \
-  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g,         \
-                     gate_slices(d), Z, d.L, d.V, d.K, d.r, cand_idx, cand_logit, zc, S)
+  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g, gate_slices(d), Z, d.L, \
+         d.V, d.K, d.r, T, seed, cycle, cand_idx, cand_logit, zc, S, jstar, qtab)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);
   } else {
@@ -180,20 +217,19 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
 }
 
 hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
-                                 const float* S, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
                                  int32_t* out_tok, hipStream_t st) {
   const dim3 grid((unsigned)d.B);
   const float* zc = reinterpret_cast<const float*>(ws + w.zc);
+  const int32_t* jstar = reinterpret_cast<const int32_t*>(ws + w.jstar);
+  const float* qtab = reinterpret_cast<const float*>(ws + w.qtab);
   const ChunkStat* stats = reinterpret_cast<const ChunkStat*>(ws + w.stats);
-  if (d.logit_dtype == DFLASH_BF16)
-    launch(trace_finalize_kernel<DFLASH_BF16>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K,
-                       w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
-                       out_tok);
-  else
-    launch(trace_finalize_kernel<DFLASH_F32>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K,
-                       w.n_chunk, T, seed, cycle, cand_idx, zc, S, path_rank, draft_tok, q, stats, accept_len,
-                       out_tok);
+#define DF_FIN(DT)                                                                                             \
+  launch(trace_finalize_kernel<DT>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K, w.n_chunk, T, seed, cycle, \
+         cand_idx, zc, jstar, qtab, path_rank, draft_tok, q, stats, accept_len, out_tok)
+  if (d.logit_dtype == DFLASH_BF16) DF_FIN(DFLASH_BF16); else DF_FIN(DFLASH_F32);
+#undef DF_FIN
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct WsLayout {
   int n_seg;    // top-K blocks per drafter row (a merge kernel runs if > 1)
   int n_chunk;  // target chunks per row
   size_t topk_partial, gate, cand_idx, cand_logit, zc, S, path_rank, draft_tok, q, stats;
+  size_t jstar, qtab;  // the fused cycle's trace table: decision and q of every row (t, i)
   size_t total;
 };
 
@@ -89,10 +90,10 @@ hipError_t launch_topk_lists(const dflash_dims& d, const WsLayout& w, const void
 hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
                                const void* W_g, const float* T, char* ws, hipStream_t st);
 hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,
-                               const void* Z, char* ws, int32_t* cand_idx, float* cand_logit, float* S,
-                               hipStream_t st);
+                               const void* Z, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                               int32_t* cand_idx, float* cand_logit, float* S, hipStream_t st);
 hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
-                                 const float* S, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
                                  int32_t* out_tok, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -202,9 +202,12 @@ struct Run {
 // reads whole 128-byte row pieces) and holds D[4 (l / 16) + v][l % 16].
 // The four waves' products are summed in wave order.  The split entry
 // point and the fused cycle both call this, so their scores are identical.
+// Returns the score S[tid / 16][tid % 16] of the calling thread (meaningful
+// where both indices are below K), so wave w holds rows 4 w .. 4 w + 3, one
+// per 16-lane group.
 template <int PT>
-__device__ __forceinline__ void edge_contract(EdgeLds& e, const void* __restrict__ E, int K, int r,
-                                              float* __restrict__ S_edge) {
+__device__ __forceinline__ float edge_contract(EdgeLds& e, const void* __restrict__ E, int K, int r,
+                                               float* __restrict__ S_edge) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = r >> 4;
   const int k0 = ((wave << 2) + (lane >> 4)) * n;
@@ -227,7 +230,9 @@ __device__ __forceinline__ void edge_contract(EdgeLds& e, const void* __restrict
   const int i = tid >> 4, j = tid & 15;
   const int ln = ((i >> 2) << 4) + j, v = i & 3;
   const float d = ((e.red[0][v][ln] + e.red[1][v][ln]) + e.red[2][v][ln]) + e.red[3][v][ln];
-  if (i < K && j < K) S_edge[i * K + j] = e.cl[j] + d;
+  const float sv = e.cl[j] + d;
+  if (i < K && j < K) S_edge[i * K + j] = sv;
+  return sv;
 }
 
 // ---------------------------------------------------------------- trace step
@@ -292,58 +297,35 @@ __device__ __forceinline__ double group_last_f64(double v, int g) {
   return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
-// NQ x 4 rows of the trace table at once (16-lane group g of the wave takes
-// rows row0 + 4 n + g, n < NQ; the NQ quads are independent, so their
-// latency chains overlap): row (t, i) holds the scores S[t][i][.] of the
-// successors of rank i at position t (LDS, K floats).  Each row gets the
-// walk's decision -- the same arithmetic as trace_step_dpp -- written to
-// jstar[row], and its q written over the scores in place.  With every row
-// decided up front, the sequential walk is only L table look-ups.
-// u[t] holds the trace uniform of position t (unused when greedy).
-template <int NQ>
-__device__ __forceinline__ void trace_rows(float* S, int row0, int n_rows, int K, float Tb, double invT,
-                                           const uint4* u, int* jstar, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  int row[NQ];
-  bool live[NQ];
-  float s[NQ], m[NQ];
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-    row[n] = row0 + 4 * n + g;
-    live[n] = row[n] < n_rows && j < K;
-    s[n] = live[n] ? S[(size_t)row[n] * K + j] : -INFINITY;
-  }
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) m[n] = __uint_as_float(group_last_u32(__float_as_uint(row16_scan_max_f32(s[n])), g));
-  int jd[NQ];
-  float qv[NQ];
+// Decision of one row (t, i) of the trace table, held by a 16-lane group
+// g of the wave: lane j of the group holds s = S[t][i][j] (live: j < K),
+// the scores of the successors of rank i at position t.  The arithmetic is
+// that of trace_step_dpp: greedy, the smallest rank attaining the maximum;
+// sampling, w = exp((s - max) / T) in fp64 (as a product with invT),
+// q = w / total, and the smallest rank whose inclusive prefix of w exceeds
+// u * total, u the trace uniform (word 0 of the (cycle, t + 1, 0) block).
+// Returns the rank for every lane of the group and sets this lane's q.
+// With every row of every position decided up front, the walk itself is
+// only L table look-ups.
+__device__ __forceinline__ int trace_row_decide(float s, bool live, int g, int j, float Tb, double invT, uint32_t u,
+                                                int K, float& qv) {
+  s = live ? s : -INFINITY;
+  const float m = __uint_as_float(group_last_u32(__float_as_uint(row16_scan_max_f32(s)), g));
+  int jd;
   if (!(Tb > 0.0f)) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const uint32_t bits = (uint32_t)(__ballot(live[n] && s[n] == m[n]) >> (16 * g)) & 0xFFFFu;
-      jd[n] = bits ? __builtin_ctz(bits) : 0;
-      qv[n] = j == jd[n] ? 1.0f : 0.0f;
-    }
+    const uint32_t bits = (uint32_t)(__ballot(live && s == m) >> (16 * g)) & 0xFFFFu;
+    jd = bits ? __builtin_ctz(bits) : 0;
+    qv = j == jd ? 1.0f : 0.0f;
   } else {
-    double w[NQ], cum[NQ];
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) w[n] = live[n] ? exp_nonpos(((double)s[n] - (double)m[n]) * invT) : 0.0;
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) cum[n] = row16_scan_f64(w[n]);
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const double total = group_last_f64(cum[n], g);
-      const double target = (double)u01_f32(u[row[n] < n_rows ? row[n] / K : 0].x) * total;
-      const uint32_t bits = (uint32_t)(__ballot(live[n] && cum[n] > target) >> (16 * g)) & 0xFFFFu;
-      jd[n] = bits ? __builtin_ctz(bits) : K - 1;
-      qv[n] = (float)(w[n] / total);
-    }
+    const double w = live ? exp_nonpos(((double)s - (double)m) * invT) : 0.0;
+    const double cum = row16_scan_f64(w);
+    const double total = group_last_f64(cum, g);
+    const double target = (double)u01_f32(u) * total;
+    const uint32_t bits = (uint32_t)(__ballot(live && cum > target) >> (16 * g)) & 0xFFFFu;
+    jd = bits ? __builtin_ctz(bits) : K - 1;
+    qv = (float)(w / total);
   }
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-    if (live[n]) S[(size_t)row[n] * K + j] = qv[n];
-    if (row[n] < n_rows && j == 0) jstar[row[n]] = jd[n];
-  }
+  return jd;
 }
 
 }  // namespace dfk

@@ -19,7 +19,7 @@
 //   fp64, runs the accept tests, and draws the residual/bonus token in two
 //   inverse-CDF levels (item = chunk or candidate, then the token inside a
 //   drawn chunk, which is re-read).  Optionally the block first walks the
-//   trace (one wave) while the other waves combine the statistics.
+//   trace over a table whose rows were decided beforehand.
 #pragma once
 
 #include "device_util.hpp"
@@ -193,7 +193,7 @@ constexpr int kTermCache = 2048;  // chunk terms of all rows kept in LDS when th
 struct FinLds {
   float2 ms[kTermCache];                            // (m, s) of every chunk of every row
   double term[kTermCache];                          // s * exp((m - M_t) / T)
-  float S[DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX];  // scores, then q of every row (trace here)
+  float S[DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX];  // q of every trace-table row (t, i)
   int jstar[DFLASH_L_MAX * DFLASH_K_MAX];           // the walk's decision for every row
   float rowM[DFLASH_L_MAX + 1];
   double rowAll[DFLASH_L_MAX + 1];                  // sum over all tokens of exp((z - M) / T)
@@ -315,14 +315,17 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
 }
 
 // One block per stream.  WITH_TRACE: the block also walks the trace over
-// scores S (wave 0) and writes path_rank / draft_tok / q; otherwise
-// path_rank and q are inputs.  zc_pre, if given, holds the candidates'
-// target logits [B, L, K] (fp32-exact values), else they are gathered here.
+// the decided trace table (jstar: decision of every row (t, i); qtab: the
+// q of every row, [B, L, K, K]) and writes path_rank / draft_tok / q;
+// otherwise path_rank and q are inputs.  zc_pre, if given, holds the
+// candidates' target logits [B, L, K] (fp32-exact values), else they are
+// gathered here.
 template <int DT, bool WITH_TRACE>
 __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, int L, int V, int K, int n_chunk,
                                 const float* __restrict__ T, const uint64_t* __restrict__ seed, uint64_t cycle,
                                 const int32_t* __restrict__ cand_idx, const float* __restrict__ zc_pre,
-                                const float* __restrict__ S, int32_t* __restrict__ path_rank,
+                                const int32_t* __restrict__ jstar, const float* __restrict__ qtab,
+                                int32_t* __restrict__ path_rank,
                                 int32_t* __restrict__ draft_tok, float* __restrict__ q,
                                 const ChunkStat* __restrict__ stats, int32_t* __restrict__ accept_len,
                                 int32_t* __restrict__ out_tok) {
@@ -354,10 +357,12 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     const int n = L * K * K;
     float sv[NS];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) sv[k] = tid + k * kFinThreads < n ? S[s0 + tid + k * kFinThreads] : 0.f;
+    for (int k = 0; k < NS; ++k) sv[k] = tid + k * kFinThreads < n ? qtab[s0 + tid + k * kFinThreads] : 0.f;
+    const int js = tid < L * K ? jstar[(size_t)b * L * K + tid] : 0;
 #pragma unroll
     for (int k = 0; k < NS; ++k)
       if (tid + k * kFinThreads < n) f.S[tid + k * kFinThreads] = sv[k];
+    if (tid < L * K) f.jstar[tid] = min(max(js, 0), K - 1);
   }
   if (!greedy) {
     if (tid >= 64 && tid < 64 + L) f.rnd0[tid - 64] = stream_block(sd, cycle, (uint32_t)(tid - 63), 0u);
@@ -377,20 +382,10 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   }
   __syncthreads();
 
-  // (1) the trace table (every row's decision, eight rows per wave task)
-  // and the per-row combination (one wave task per target row), spread over
-  // the waves
-  {
-    const int n_rows = WITH_TRACE ? L * K : 0;
-    const int n_oct = (n_rows + 7) / 8;
-    for (int task = wave; task < n_oct + L + 1; task += kFinWaves) {
-      if (task < n_oct)
-        trace_rows<2>(f.S, task * 8, n_rows, K, Tb, invT, f.rnd0, f.jstar, lane);
-      else
-        combine_row<DT>(f, st_all + (size_t)(task - n_oct) * n_chunk, task - n_oct, L, K, n_chunk, cached,
-                        greedy, invT, lane);
-    }
-  }
+  // (1) the per-row combination of the chunk statistics, one wave per
+  // target row
+  for (int t = wave; t <= L; t += kFinWaves)
+    combine_row<DT>(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, greedy, invT, lane);
   __syncthreads();
   if (WITH_TRACE) {
     // the walk from rank 0: L look-ups; then the chosen rows' q, ranks and

@@ -410,18 +410,16 @@ __device__ __forceinline__ void merge_row(const uint64_t* __restrict__ lists, in
   __syncthreads();
 }
 
-// Merge the lists of rows r0 and r1 (global; r0 may be absent: n0 = 0) into
-// out0 / out1 (LDS, K entries each) in one pass; `keys` holds at least
-// 2 * n_seg * 16 entries.  Every thread of the block takes part; ends with
-// a barrier.
-__device__ __forceinline__ void merge_two_rows(const uint64_t* __restrict__ lists0, bool has0,
-                                               const uint64_t* __restrict__ lists1, int n_seg, int K, uint64_t* keys,
-                                               uint64_t* out0, uint64_t* out1) {
+// Merge the sorted lists of two rows, staged in `keys` (LDS, barrier
+// passed: n_seg lists of 16 keys of row r0, then n_seg lists of row r1;
+// zeros for an absent row), into out0 / out1 (LDS, K entries each) in one
+// pass: each key's rank is its position in its own list plus the count of
+// greater keys in the row's other lists.  Every thread of the block takes
+// part; ends with a barrier.
+__device__ __forceinline__ void merge_two_staged(const uint64_t* keys, int n_seg, int K, uint64_t* out0,
+                                                 uint64_t* out1) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int nk = n_seg * 16;
-  for (int i = tid; i < 2 * nk; i += nt)
-    keys[i] = i < nk ? (has0 ? lists0[i] : 0ull) : lists1[i - nk];
-  __syncthreads();
   for (int i = tid; i < 2 * nk; i += nt) {
     const int half = i >= nk, j = i - half * nk;
     const int s = j >> 4, k = j & 15;

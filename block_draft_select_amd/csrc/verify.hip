@@ -30,8 +30,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
   __shared__ FinLds f;
   finalize_stream<DT, false>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, nullptr, nullptr,
-                             const_cast<int32_t*>(path_rank), nullptr, const_cast<float*>(q), stats, accept_len,
-                             out_tok);
+                             nullptr, const_cast<int32_t*>(path_rank), nullptr, const_cast<float*>(q), stats,
+                             accept_len, out_tok);
 }
 
 }  // namespace
