@@ -91,6 +91,27 @@ def test_full_size_configs_sampled(name, cid, streams):
         compare_stream(gpu, ref[b], b)
 
 
+# limits of the boundary: every token a candidate (the residual has no
+# chunk mass), the largest vocabulary (more chunk terms than the finalize
+# keeps in LDS), and the largest row count B (L + 1) = 65535
+EXTREME = [
+    ("bf16-V-eq-K", 3, dict(B=3, V=16, K=16, hidden=256, plant=None), None),
+    ("f32-V-eq-K4", 1, dict(B=2, V=4, K=4, T=0.8), None),
+    ("bf16-max-V", 3, dict(B=1, L=4, V=2097152, hidden=256, plant=None), None),
+    ("bf16-max-rows", 3, dict(B=3855, L=16, V=64, hidden=16, r=16, plant=None), [0, 1, 1927, 3854]),
+]
+
+
+@pytest.mark.parametrize("name,cid,kw,streams", EXTREME, ids=[c[0] for c in EXTREME])
+def test_extreme_shapes(name, cid, kw, streams):
+    inp = synth.make(cid, set_id=9, **kw)
+    _say(f"[parity] extreme {name}: B={inp['B']} L={inp['L']} V={inp['V']} K={inp['K']}")
+    ref, _ = guarded(inp, streams=streams)
+    gpu = run_cycle(inp)
+    for b in ref:
+        compare_stream(gpu, ref[b], b)
+
+
 def test_split_entry_points_equal_cycle():
     import torch
     import block_draft_select_amd as dfl
