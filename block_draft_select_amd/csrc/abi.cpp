@@ -172,7 +172,7 @@ WsLayout ws_layout(const dflash_dims& d) {
   w.n_chunk = (d.V + kChunk - 1) / kChunk;
   size_t o = 0;
   w.topk_partial = o; o = align256(o + R * w.n_seg * 16 * sizeof(uint64_t));
-  w.gate = o;         o = align256(o + (size_t)gate_slices(d) * R * d.r * sizeof(float));
+  w.gate = o;         o = align256(o + (size_t)gate_groups(d) * R * d.r * sizeof(float));
   w.cand_idx = o;     o = align256(o + R * d.K * sizeof(int32_t));
   w.cand_logit = o;   o = align256(o + R * d.K * sizeof(float));
   w.zc = o;           o = align256(o + R * d.K * sizeof(float));

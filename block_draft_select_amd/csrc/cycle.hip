@@ -1,10 +1,10 @@
 // dflash_cycle: the whole draft -> select -> verify cycle in three launches
 // on the caller's stream.
 //   1. stream_kernel: one grid streams every logit once.  Its first blocks
-//      fold the drafter rows into sorted top lists (S1), the next ones
-//      reduce the target rows to chunk statistics (S5), the last ones
-//      compute the gate's hidden-slice partials (S2; they depend only on h
-//      and W_g).  Nothing in the launch waits on anything else in it.
+//      compute the gate's pre-activation tiles (S2; they depend only on h
+//      and W_g), the next ones fold the drafter rows into sorted top lists
+//      (S1), the last ones reduce the target rows to chunk statistics (S5).
+//      Nothing in the launch waits on anything else in it.
 //   2. cand_scores_kernel: one block per edge (b, t) merges the top lists of
 //      rows t-1 and t, writes row t's candidates (and their target logits),
 //      computes the edge's pair scores (S2, S3), and decides the edge's K
@@ -30,22 +30,45 @@ union StreamLds {
   float red[kGateRed];
 };
 
+constexpr bool kGateFirst = true;
+
+// gate block gi -> (row tile, column tile, group of hidden slices), group fastest
+template <int PT>
+__device__ __forceinline__ void gate_block(const void* __restrict__ h, const void* __restrict__ W, int R, int H, int r,
+                                           float* __restrict__ gpart, int gate_cols, int n_ks, int gi, float* red) {
+  if (PT == DFLASH_BF16) {
+    const int n_grp = (n_ks + kGateGroup - 1) / kGateGroup;
+    const int g = gi % n_grp, tile = gi / n_grp;
+    gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
+                      tile / gate_cols, tile - (tile / gate_cols) * gate_cols, g * kGateGroup,
+                      min(kGateGroup, n_ks - g * kGateGroup), red);
+  } else {
+    gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, gpart, gi);
+  }
+}
+
 template <int DT, int PT>
 __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U, const void* __restrict__ Z, int R,
                                                      int V, int K, int L, int n_sub, int spb, int n_seg,
                                                      uint64_t* __restrict__ partial, int n_chunk, int n_grp,
                                                      const float* __restrict__ T, ChunkStat* __restrict__ stats,
                                                      const void* __restrict__ h, const void* __restrict__ W, int H,
-                                                     int r, float* __restrict__ gpart, int gate_cols, int n_ks) {
+                                                     int r, float* __restrict__ gpart, int gate_cols, int n_ks,
+                                                     int n_gate) {
   __shared__ StreamLds sh;
-  // top-K blocks in drafter-row order, then statistics blocks in target-row
-  // order: the whole grid sweeps U and then Z front to back (measured ~10%
-  // faster than interleaving the two kinds, which splits the reads between
-  // two distant regions).  The gate blocks come last and run in the
-  // launch's tail, where the sweep no longer fills the machine (in front
-  // they held slots while the sweep started: measured ~3 us slower; placed
-  // anywhere inside the statistics part, 1.3 to 2.2 us slower).
+  // gate blocks first (few and long: each accumulates up to kGateGroup
+  // hidden slices of its tile), then top-K blocks in drafter-row order, then
+  // statistics blocks in target-row order: the grid sweeps U and then Z
+  // front to back (measured ~10% faster than interleaving the two kinds,
+  // which splits the reads between two distant regions)
   int id = blockIdx.x;
+  if (kGateFirst) {
+    if (id < n_gate) {
+      gate_block<PT>(h, W, R, H, r, gpart, gate_cols, n_ks, id, sh.red);
+      return;
+    }
+    id -= n_gate;
+  }
   const int n_topk = R * n_seg;
   if (id < n_topk) {
     const int row = id / n_seg, seg = id - row * n_seg;
@@ -55,16 +78,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ U,
   }
   id -= n_topk;
   const int n_stat = (R / L) * (L + 1) * n_grp;
-  if (id >= n_stat) {
-    const int gi = id - n_stat;
-    if (PT == DFLASH_BF16) {
-      // gate block gi -> (row tile, column tile, hidden slice), slice fastest
-      const int ks = gi % n_ks, tile = gi / n_ks;
-      gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
-                        tile / gate_cols, tile - (tile / gate_cols) * gate_cols, ks, sh.red);
-    } else {
-      gate_row_f32(reinterpret_cast<const float*>(h), reinterpret_cast<const float*>(W), H, r, gpart, gi);
-    }
+  if (!kGateFirst && id >= n_stat) {
+    gate_block<PT>(h, W, R, H, r, gpart, gate_cols, n_ks, id - n_stat, sh.red);
     return;
   }
   const int rowid = id / n_grp;
@@ -177,7 +192,7 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
   const int n_grp = (w.n_chunk + 3) / 4;
   const int gate_cols = (d.r + kGateCols - 1) / kGateCols;
   const int n_ks = gate_slices(d);
-  const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols * n_ks : R;
+  const int n_gate = d.param_dtype == DFLASH_BF16 ? ((R + 15) / 16) * gate_cols * gate_groups(d) : R;
   const long long blocks = (long long)R * w.n_seg + (long long)d.B * (d.L + 1) * n_grp + n_gate;
   uint64_t* partial = reinterpret_cast<uint64_t*>(ws + w.topk_partial);
   ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws + w.stats);
@@ -185,7 +200,7 @@ hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const vo
 #define DF_STREAM(DT, PT)                                                                                     \
   launch((stream_kernel<DT, PT>), dim3((unsigned)blocks), dim3(256), st, U, Z, R, d.V, d.K,   \
                      d.L, w.n_sub, w.spb, w.n_seg, partial, w.n_chunk, n_grp, T, stats, h, W_g, d.hidden, d.r, \
-                     gpart, gate_cols, n_ks)
+                     gpart, gate_cols, n_ks, n_gate)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_STREAM(DFLASH_BF16, DFLASH_BF16); else DF_STREAM(DFLASH_BF16, DFLASH_F32);
   } else {
@@ -205,7 +220,7 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
   int32_t* jstar = reinterpret_cast<int32_t*>(ws + w.jstar);
   float* qtab = reinterpret_cast<float*>(ws + w.qtab);
 #define DF_SCORES(DT, PT)                                                                                      \
-  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g, gate_slices(d), Z, d.L, \
+  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g, gate_groups(d), Z, d.L, \
          d.V, d.K, d.r, T, seed, cycle, cand_idx, cand_logit, zc, S, jstar, qtab)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);

@@ -27,13 +27,16 @@ constexpr int kTopkMaxSeg = kTopkCycleMerge / 16;
 
 constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
 
-// gate: the hidden dimension is cut into slices of kGateSlice; each slice's
-// partial pre-activation W_g h is its own small MFMA block, and consumers
-// sum the slices in slice order before the sigmoid
+// gate: the hidden dimension is cut into slices of kGateSlice; a gate block
+// accumulates kGateGroup consecutive slices of one tile on the matrix
+// cores, and consumers sum the groups' partial pre-activations W_g h in
+// group order before the sigmoid
 constexpr int kGateSlice = 256;
+constexpr int kGateGroup = 8;
 inline int gate_slices(const dflash_dims& d) {
   return d.param_dtype == DFLASH_BF16 ? (d.hidden + kGateSlice - 1) / kGateSlice : 1;
 }
+inline int gate_groups(const dflash_dims& d) { return (gate_slices(d) + kGateGroup - 1) / kGateGroup; }
 
 struct ChunkStat {
   float m;      // chunk maximum logit

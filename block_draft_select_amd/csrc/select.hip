@@ -9,11 +9,12 @@ namespace dfk {
 
 namespace {
 
-// grid (row tiles, column tiles, hidden slices)
+// grid (row tiles, column tiles, groups of hidden slices)
 __global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                         int R, int H, int r, float* __restrict__ part) {
   __shared__ float red[kGateRed];
-  gate_partial_bf16(h, W, R, H, r, part, blockIdx.x, blockIdx.y, blockIdx.z, red);
+  const int n_ks = (H + kGateSlice - 1) / kGateSlice, ks0 = blockIdx.z * kGateGroup;
+  gate_partial_bf16(h, W, R, H, r, part, blockIdx.x, blockIdx.y, ks0, min(kGateGroup, n_ks - ks0), red);
 }
 
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(64) void trace_kernel(const float* __restrict__ S, 
 hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* gpart, hipStream_t st) {
   const int R = d.B * d.L;
   if (d.param_dtype == DFLASH_BF16) {
-    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols), (unsigned)gate_slices(d));
+    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols), (unsigned)gate_groups(d));
     launch(gate_mfma_kernel, grid, dim3(256), st, reinterpret_cast<const uint16_t*>(h),
                        reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, gpart);
   } else {
@@ -108,7 +109,7 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
                          const float* cand_logit, const void* E, const float* gpart, float* S,
                          hipStream_t st) {
   const dim3 grid((unsigned)(d.B * d.L));
-  const int n_ks = gate_slices(d);
+  const int n_ks = gate_groups(d);
   if (d.param_dtype == DFLASH_BF16)
     launch(scores_kernel<DFLASH_BF16>, grid, dim3(256), st, x0, cand_idx, cand_logit, E, gpart,
                        n_ks, d.L, d.V, d.K, d.r, S);

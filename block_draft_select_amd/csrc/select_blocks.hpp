@@ -23,57 +23,60 @@ constexpr int kGateRed = kGateWaves * kGateCT * 4 * 64;  // floats of LDS per ga
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Partial pre-activation of one 16-row x 32-column tile of W_g h over
-// hidden slice ks ([ks * 256, ks * 256 + 256) of the hidden dimension):
-// part[ks][row][col] = sum over the slice of h[row][k] W_g[col][k].  Wave w
-// takes the contiguous quarter [64 w, 64 w + 64) of the slice as two
-// v_mfma_f32_16x16x32_bf16 steps per 16-column tile; every operand load is
-// issued before the first MFMA, so a block waits on memory once, and each
+// Partial pre-activation of one 16-row x 32-column tile of W_g h over the
+// hidden slices ks0 .. ks0 + n_sl - 1 (slice ks = [ks * 256, ks * 256 + 256)
+// of the hidden dimension): part[grp][row][col] = sum over those slices of
+// h[row][k] W_g[col][k], grp = ks0 / kGateGroup.  In each slice wave w takes
+// the contiguous quarter [64 w, 64 w + 64) as two v_mfma_f32_16x16x32_bf16
+// steps per 16-column tile, accumulating across the slices in slice order;
+// a slice's operand loads are all issued before its first MFMA, and each
 // wave reads 128 contiguous bytes of every row it touches.  The four
 // waves' tiles are summed through `red` (LDS) in wave order.  Operand
 // layout: lane l holds A[l % 16][8 (l / 16) + 0..7] and
 // B[8 (l / 16) + 0..7][l % 16] (one 16-byte load each, A = h and
 // B[k][n] = W_g[n][k], both contiguous along k); the accumulator holds
-// D[4 (l / 16) + i][l % 16].  A hidden slice shorter than 256 (hidden is a
+// D[4 (l / 16) + i][l % 16].  A slice shorter than 256 (hidden is a
 // multiple of 16) zero-fills the 8-element groups past its end.
 __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                   int R, int H, int r, float* __restrict__ part, int tile_row,
-                                                  int tile_col, int ks, float* red) {
+                                                  int tile_col, int ks0, int n_sl, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = tile_row * 16, col0 = tile_col * kGateCols;
-  const int kend = min(H, ks * kGateSlice + kGateSlice);
-  const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;  // this lane's first k
   const int arow = row0 + (lane & 15);
-  const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
   const int col = col0 + (lane & 15);
-  const uint16_t* wp = W + kw;
-  constexpr int kSteps = kGateSlice / kGateWaves / 32;  // 32-wide k-steps per wave
+  constexpr int kSteps = kGateSlice / kGateWaves / 32;  // 32-wide k-steps per wave and slice
   const bf16x8 zero = {};
-  bf16x8 a[kSteps], bv[kSteps][kGateCT];
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const bool ok = kw + 32 * i < kend;
-    a[i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
-#pragma unroll
-    for (int ct = 0; ct < kGateCT; ++ct) {
-      const int c = col + ct * 16;
-      bv[i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
-    }
-  }
   v4f32 acc[kGateCT];
 #pragma unroll
   for (int ct = 0; ct < kGateCT; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
+  for (int ks = ks0; ks < ks0 + n_sl; ++ks) {
+    const int kend = min(H, ks * kGateSlice + kGateSlice);
+    const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;  // this lane's first k
+    const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
+    const uint16_t* wp = W + kw;
+    bf16x8 a[kSteps], bv[kSteps][kGateCT];
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i)
+    for (int i = 0; i < kSteps; ++i) {
+      const bool ok = kw + 32 * i < kend;
+      a[i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
 #pragma unroll
-    for (int ct = 0; ct < kGateCT; ++ct)
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[i][ct], acc[ct], 0, 0, 0);
+      for (int ct = 0; ct < kGateCT; ++ct) {
+        const int c = col + ct * 16;
+        bv[i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+      for (int ct = 0; ct < kGateCT; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[i][ct], acc[ct], 0, 0, 0);
+  }
 #pragma unroll
   for (int ct = 0; ct < kGateCT; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((wave * kGateCT + ct) * 4 + i) * kWave + lane] = acc[ct][i];
   __syncthreads();
-  float* out = part + (size_t)ks * R * r;
+  float* out = part + (size_t)(ks0 / kGateGroup) * R * r;
 #pragma unroll
   for (int o2 = 0; o2 < kGateCT; ++o2) {
     const int o = tid + o2 * 256;
@@ -100,8 +103,8 @@ __device__ __forceinline__ void gate_row_f32(const float* __restrict__ h, const 
   part[(size_t)row * r + col] = acc;
 }
 
-// g = sigmoid(sum of the slice partials, in slice order) for one column of
-// row `row`; `stride` = rows * r (the distance between slices)
+// g = sigmoid(sum of the slice-group partials, in group order) for one
+// column of row `row`; `stride` = rows * r (the distance between groups)
 __device__ __forceinline__ float gate_value(const float* __restrict__ part, int n_ks, size_t stride, int row, int r,
                                             int col) {
   const float* p = part + (size_t)row * r + col;
