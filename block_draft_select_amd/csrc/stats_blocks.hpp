@@ -383,35 +383,54 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   __syncthreads();
 
   // (1) the per-row combination of the chunk statistics, one wave per
-  // target row
-  for (int t = wave; t <= L; t += kFinWaves)
-    combine_row<DT>(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, greedy, invT, lane);
-  __syncthreads();
-  if (WITH_TRACE) {
-    // the walk from rank 0: L look-ups; then the chosen rows' q, ranks and
-    // tokens
-    if (wave == 0) {
-      int prev = 0;
-      for (int t = 0; t < L; ++t) {
-        prev = f.jstar[t * K + prev];
-        if (lane == 0) f.rank[t] = prev;
+  // target row; with the trace, wave 0 meanwhile walks the decided table
+  // from rank 0 (L look-ups) and copies out each position's q (the row of
+  // its predecessor's rank), rank and token
+  if (WITH_TRACE && wave == 0) {
+    // the table's decisions in registers (lane l holds rows l, l + 64, ...)
+    // so that each step of the chain is a lane read, not an LDS round trip
+    constexpr int NJ = DFLASH_L_MAX * DFLASH_K_MAX / kWave;
+    int jv[NJ];
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) jv[c] = lane + c * kWave < L * K ? f.jstar[lane + c * kWave] : 0;
+    int prev = 0, mine = 0, pred = 0;  // lane t keeps rank t and its predecessor's rank
+    for (int t = 0; t < L; ++t) {
+      const int row = t * K + prev;
+      int next = 0;
+#pragma unroll
+      for (int c = 0; c < NJ; ++c)
+        if ((row >> 6) == c) next = __builtin_amdgcn_readlane(jv[c], row & 63);
+      if (lane == t) {
+        pred = prev;
+        mine = next;
+      }
+      prev = next;
+    }
+    if (lane < L) {
+      f.rank[lane] = mine;
+      path_rank[(size_t)b * L + lane] = mine;
+      draft_tok[(size_t)b * L + lane] = f.cand[lane][mine];
+    }
+    // q of position t is the row of its predecessor's rank (rank 0 at t =
+    // 0); every lane takes part in every lane exchange
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) {
+      const int i = lane + c * kWave;
+      const bool ok = i < L * K;
+      const int t = ok ? i / K : 0, j = i - t * K;
+      const int pr = __shfl(pred, t);
+      if (ok) {
+        const float qv = f.S[(t * K + pr) * K + j];
+        f.qs[t][j] = qv;
+        q[(size_t)b * L * K + i] = qv;
       }
     }
-    __syncthreads();
-    for (int i = tid; i < L * K; i += kFinThreads) {
-      const int t = i / K, j = i - (i / K) * K;
-      const int rk = f.rank[t];
-      // q of position t is the row of the predecessor's rank (rank 0 at t = 0)
-      const float qv = f.S[(t * K + (t > 0 ? f.rank[t - 1] : 0)) * K + j];
-      f.qs[t][j] = qv;
-      q[(size_t)b * L * K + i] = qv;
-      if (j == 0) {
-        path_rank[(size_t)b * L + t] = rk;
-        draft_tok[(size_t)b * L + t] = f.cand[t][rk];
-      }
-    }
-    __syncthreads();
+  } else {
+    constexpr int w0 = WITH_TRACE ? 1 : 0;
+    for (int t = wave - w0; t <= L; t += kFinWaves - w0)
+      combine_row<DT>(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, greedy, invT, lane);
   }
+  __syncthreads();
 
   const size_t o = (size_t)b * (L + 1);
   if (greedy) {
