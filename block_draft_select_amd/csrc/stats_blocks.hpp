@@ -207,7 +207,7 @@ struct FinLds {
   uint4 rnd1[DFLASH_L_MAX + 1];                     // (cycle, t + 1, 1) blocks
   int pick_row[DFLASH_L_MAX + 1];                   // first-level draw of every row
   double wave_tot[kFinWaves];
-  int s_n, s_tok, s_last;
+  int s_n;
 };
 
 // Combine the statistics of row t (one wave): maximum, first argmax chunk,
@@ -455,11 +455,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       rejected = !(u * (double)f.qs[lane][j] < p);
     }
     const int fl = first_lane(rejected);
-    if (lane == 0) {
-      f.s_n = fl < L ? fl : L;
-      f.s_tok = 0x7FFFFFFF;
-      f.s_last = -1;
-    }
+    if (lane == 0) f.s_n = fl < L ? fl : L;
   } else {
     for (int t = wave - 1; t <= L; t += kFinWaves - 1) {
       const int pk = pick_item(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, invT, lane);
@@ -504,31 +500,47 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     const double incl = wave_scan_f64(run);
     if (lane == kWave - 1) f.wave_tot[wave] = incl;
     __syncthreads();
-    double base = incl - run;
-    for (int w = 0; w < wave; ++w) base += f.wave_tot[w];
-    double total = 0.0;
-    for (int w = 0; w < kFinWaves; ++w) total += f.wave_tot[w];
+    // Every wave forms the same inclusive prefix sums P_w of the wave
+    // totals (one lane per wave, a row scan) and so agrees on the owner:
+    // the first wave with P_w > u2 * P_last.  Only the owner looks for the
+    // token (the first of its values whose cumulative mass exceeds the
+    // target; its last positive value if rounding leaves none) and writes
+    // the outputs, so no second barrier is needed.  If no prefix exceeds
+    // the target (rounding at the very end), the last wave with mass takes
+    // its last positive value; with no mass at all, wave 0 takes the
+    // chunk's first token.
+    static_assert(kFinWaves == 16, "one row of lanes per wave total");
+    const double tw = lane < kFinWaves ? f.wave_tot[lane] : 0.0;
+    const double P = row16_scan_f64(tw);
+    const double total = readlane_f64(P, kFinWaves - 1);
     const double target = u01_f64(w1.z, w1.w) * total;
+    const uint64_t over = __ballot(lane < kFinWaves && P > target);
+    const uint64_t mass = __ballot(lane < kFinWaves && tw > 0.0);
+    const int owner = over ? __builtin_ctzll(over) : -1;
+    const int lastw = mass ? 63 - __builtin_clzll(mass) : -1;
+    const double before = owner > 0 ? readlane_f64(P, owner - 1) : 0.0;
+    const int taker = owner >= 0 ? owner : (lastw >= 0 ? lastw : 0);
+    if (wave != taker) return;
     int first = 0x7FFFFFFF;
+    if (owner >= 0) {
+      const double base = before + (incl - run);
 #pragma unroll
-    for (int i = kFinTpt - 1; i >= 0; --i)
-      if (base + wv[i] > target) first = e0 + i;
-    // tokens follow the lane order, so the wave's smallest hit is in its
-    // lowest hitting lane and its last positive weight in its highest lane:
-    // one LDS atomic per wave
+      for (int i = kFinTpt - 1; i >= 0; --i)
+        if (base + wv[i] > target) first = e0 + i;
+    }
+    // tokens follow the lane order: the wave's smallest hit is in its
+    // lowest hitting lane, its last positive value in its highest lane
     const uint64_t hit = __ballot(first != 0x7FFFFFFF);
     const uint64_t pos = __ballot(last_pos >= 0);
-    if (hit) {
-      const int v = __builtin_amdgcn_readlane(first, __builtin_ctzll(hit));
-      if (lane == 0) atomicMin(&f.s_tok, v);
-    }
-    if (pos) {
-      const int v = __builtin_amdgcn_readlane(last_pos, 63 - __builtin_clzll(pos));
-      if (lane == 0) atomicMax(&f.s_last, v);
-    }
-    __syncthreads();
-    tok = f.s_tok;
-    if (tok == 0x7FFFFFFF) tok = f.s_last >= 0 ? f.s_last : min(V - 1, c0);
+    if (hit)
+      tok = __builtin_amdgcn_readlane(first, __builtin_ctzll(hit));
+    else if (pos)
+      tok = __builtin_amdgcn_readlane(last_pos, 63 - __builtin_clzll(pos));
+    else
+      tok = min(V - 1, c0);
+    if (lane <= L) out_tok[o + lane] = lane < ts ? f.cand[lane][f.rank[lane]] : (lane == ts ? tok : -1);
+    if (lane == 0) accept_len[b] = ts;
+    return;
   }
   if (tid == 0) {
     accept_len[b] = ts;
