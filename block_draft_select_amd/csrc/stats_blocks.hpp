@@ -258,14 +258,10 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
   const int nk = t < L ? K : 0;
   const double inv = 1.0 / f.rowAll[t];
   const uint4 w1 = f.rnd1[t];
-  // the row's candidates in registers: their chunk and weight
+  // the chunk of each of the row's candidates, in registers
   int cchunk[DFLASH_K_MAX];
-  double cpc[DFLASH_K_MAX];
 #pragma unroll
-  for (int k = 0; k < DFLASH_K_MAX; ++k) {
-    cchunk[k] = k < nk ? f.cand[t][k] / kChunk : -1;
-    cpc[k] = k < nk ? f.pc[t][k] : 0.0;
-  }
+  for (int k = 0; k < DFLASH_K_MAX; ++k) cchunk[k] = k < nk ? f.cand[t][k] / kChunk : -1;
   const int n_item = n_chunk + nk;
   auto item = [&](int i, bool resid) -> double {
     if (i < n_chunk) {
@@ -276,10 +272,16 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
         const ChunkStat cs = st[i];
         tm = (double)cs.s * exp_nonpos(((double)cs.m - (double)f.rowM[t]) * invT);
       }
-      double cm = 0.0;
+      // the weights of the candidates inside chunk i, added in candidate
+      // order (integer matching first: a chunk rarely holds more than one)
+      uint32_t m = 0;
 #pragma unroll
-      for (int k = 0; k < DFLASH_K_MAX; ++k)
-        if (k < nk && cchunk[k] == i) cm += cpc[k];
+      for (int k = 0; k < DFLASH_K_MAX; ++k) m |= (cchunk[k] == i ? 1u : 0u) << k;
+      double cm = 0.0;
+      while (m) {
+        cm += f.pc[t][__builtin_ctz(m)];
+        m &= m - 1u;
+      }
       return fmax(0.0, (tm - cm) * inv);
     }
     if (i < n_item) {
