@@ -254,7 +254,7 @@ __device__ __forceinline__ void combine_row(FinLds& f, const ChunkStat* __restri
 // residual has no mass the candidates keep mass p instead.  Items past the
 // first 64 are recomputed in a second pass rather than stored.
 __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __restrict__ st, int t, int L, int K,
-                                         int n_chunk, bool cached, double invT, int lane) {
+                                         int n_chunk, bool cached, double invT, const float* qrow, int lane) {
   const int nk = t < L ? K : 0;
   const double inv = 1.0 / f.rowAll[t];
   const uint4 w1 = f.rnd1[t];
@@ -286,7 +286,7 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
     }
     if (i < n_item) {
       const double p = f.pc[t][i - n_chunk] * inv;
-      return resid ? fmax(0.0, p - (double)f.qs[t][i - n_chunk]) : p;
+      return resid ? fmax(0.0, p - (double)qrow[i - n_chunk]) : p;
     }
     return 0.0;
   };
@@ -314,6 +314,14 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
     carry = readlane_f64(v, 63);
   }
   return n_item - 1;
+}
+
+// q of position t (t < L, K values in LDS): with the trace, the table row of
+// its predecessor's rank (rank 0 at t = 0); else the q the caller passed
+template <bool WITH_TRACE>
+__device__ __forceinline__ const float* q_row_of(const FinLds& f, int t, int K) {
+  if (WITH_TRACE) return &f.S[(t * K + (t > 0 ? f.rank[t - 1] : 0)) * K];
+  return f.qs[t];
 }
 
 // One block per stream.  WITH_TRACE: the block also walks the trace over
@@ -395,37 +403,23 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     int jv[NJ];
 #pragma unroll
     for (int c = 0; c < NJ; ++c) jv[c] = lane + c * kWave < L * K ? f.jstar[lane + c * kWave] : 0;
-    int prev = 0, mine = 0, pred = 0;  // lane t keeps rank t and its predecessor's rank
+    int prev = 0, mine = 0;  // lane t keeps rank t
     for (int t = 0; t < L; ++t) {
+      // every block's lane read, then a scalar select: no branch per step
       const int row = t * K + prev;
       int next = 0;
 #pragma unroll
-      for (int c = 0; c < NJ; ++c)
-        if ((row >> 6) == c) next = __builtin_amdgcn_readlane(jv[c], row & 63);
-      if (lane == t) {
-        pred = prev;
-        mine = next;
+      for (int c = 0; c < NJ; ++c) {
+        const int v = __builtin_amdgcn_readlane(jv[c], row & 63);
+        next = (row >> 6) == c ? v : next;
       }
+      if (lane == t) mine = next;
       prev = next;
     }
     if (lane < L) {
       f.rank[lane] = mine;
       path_rank[(size_t)b * L + lane] = mine;
       draft_tok[(size_t)b * L + lane] = f.cand[lane][mine];
-    }
-    // q of position t is the row of its predecessor's rank (rank 0 at t =
-    // 0); every lane takes part in every lane exchange
-#pragma unroll
-    for (int c = 0; c < NJ; ++c) {
-      const int i = lane + c * kWave;
-      const bool ok = i < L * K;
-      const int t = ok ? i / K : 0, j = i - t * K;
-      const int pr = __shfl(pred, t);
-      if (ok) {
-        const float qv = f.S[(t * K + pr) * K + j];
-        f.qs[t][j] = qv;
-        q[(size_t)b * L * K + i] = qv;
-      }
     }
   } else {
     constexpr int w0 = WITH_TRACE ? 1 : 0;
@@ -434,6 +428,14 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   }
   __syncthreads();
 
+  // the q output of the trace: the row of each position's predecessor's
+  // rank, written by the last wave (idle or nearly so in the next phase)
+  if (WITH_TRACE && wave == kFinWaves - 1) {
+    for (int i = lane; i < L * K; i += kWave) {
+      const int t = i / K;
+      q[(size_t)b * L * K + i] = q_row_of<WITH_TRACE>(f, t, K)[i - t * K];
+    }
+  }
   const size_t o = (size_t)b * (L + 1);
   if (greedy) {
     if (tid == 0) {
@@ -454,13 +456,14 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       const int j = f.rank[lane];
       const double u = (double)u01_f32(f.rnd0[lane].y);
       const double p = f.pc[lane][j] / f.rowAll[lane];
-      rejected = !(u * (double)f.qs[lane][j] < p);
+      rejected = !(u * (double)q_row_of<WITH_TRACE>(f, lane, K)[j] < p);
     }
     const int fl = first_lane(rejected);
     if (lane == 0) f.s_n = fl < L ? fl : L;
   } else {
     for (int t = wave - 1; t <= L; t += kFinWaves - 1) {
-      const int pk = pick_item(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, invT, lane);
+      const int pk = pick_item(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, invT,
+                               t < L ? q_row_of<WITH_TRACE>(f, t, K) : f.qs[0], lane);
       if (lane == 0) f.pick_row[t] = pk;
     }
   }
