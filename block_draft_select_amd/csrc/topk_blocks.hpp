@@ -426,9 +426,31 @@ __device__ __forceinline__ void merge_two_staged(const uint64_t* keys, int n_seg
     const uint64_t key = keys[i];
     if (key == 0ull || k >= K) continue;
     const uint64_t* base = keys + half * nk;
+    // the other lists' counts: eight binary searches at a time, level by
+    // level, so each level's eight loads are in flight together
     int rank = k;
-    for (int s2 = 0; s2 < n_seg && rank < K; ++s2)
-      if (s2 != s) rank += count_greater16(base + s2 * 16, key);
+    for (int g0 = 0; g0 < n_seg; g0 += 8) {
+      const uint64_t* lp[8];
+      int lo[8];
+      bool l15[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        lp[q] = base + min(g0 + q, n_seg - 1) * 16;
+        l15[q] = lp[q][15] > key;
+        lo[q] = lp[q][7] > key ? 8 : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q] + 3] > key ? 4 : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q] + 1] > key ? 2 : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q]] > key ? 1 : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int s2 = g0 + q;
+        if (s2 < n_seg && s2 != s) rank += lo[q] == 15 && l15[q] ? 16 : lo[q];
+      }
+    }
     if (rank < K) (half ? out1 : out0)[rank] = key;
   }
   __syncthreads();
