@@ -127,7 +127,7 @@ def main():
 
     if args.gpus != 1:
         sys.exit(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-                 "(the batch of streams shards by stream across GPUs with no exchange; see DESIGN.md)")
+                 "(the batch of streams would shard by stream across GPUs, with no exchange)")
 
     import torch
     import synth

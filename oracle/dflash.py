@@ -22,7 +22,7 @@ C_t is the ordered list of K candidates at position t.  E is the [V, r]
 candidate-embedding table and W the [r, hidden] gate matrix (one row per
 embedding dimension, the layout of a linear layer's weight).
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
   * score:   s_t(a, b) = U_t(b) + sum_k E[a,k] * g_t[k] * E[b,k],
              g_t = sigmoid(W @ h_t)  (the formula itself was lost from P3);
   * edge 1 uses a = x0 for every row of its score matrix;
