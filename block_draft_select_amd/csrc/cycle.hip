@@ -134,32 +134,26 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
     if (tid + q * 256 < 2 * nk) cl.keys[tid + q * 256] = kv[q];
   __syncthreads();
   merge_two_staged(cl.keys, n_seg, K, cl.prev, cl.cur);
-  if (tid < 16) {
-    int p = -1, c = -1;
-    float v = 0.f;
-    if (tid < K) {
-      p = t == 0 ? clamp_idx(x0[b], V) : key_index(cl.prev[tid]);
-      c = key_index(cl.cur[tid]);
-      v = key_value(cl.cur[tid]);
-      const size_t o = (size_t)bt * K + tid;
-      cand_idx[o] = c;
-      cand_logit[o] = v;
-    } else if (t == 0) {
-      p = clamp_idx(x0[b], V);
-    }
-    cl.e.pidx[tid] = p;
-    cl.e.cidx[tid] = c;
-    cl.e.cl[tid] = v;
+  // every thread reads the merged lists itself (no second hand-off):
+  // the tokens of row lane % 16 (its MFMA operands) and the logit of
+  // candidate tid % 16 (its score's column)
+  const int rl = tid & 15;
+  const int pl = rl < K ? (t == 0 ? clamp_idx(x0[b], V) : key_index(cl.prev[rl])) : (t == 0 ? clamp_idx(x0[b], V) : -1);
+  const int cidx_l = rl < K ? key_index(cl.cur[rl]) : -1;
+  const float cl_j = rl < K ? key_value(cl.cur[rl]) : 0.f;
+  if (tid < K) {
+    const size_t o = (size_t)bt * K + tid;
+    cand_idx[o] = cidx_l;
+    cand_logit[o] = cl_j;
   }
-  __syncthreads();
   // the candidates' target logits are gathered while the embedding rows load
   float zv = 0.f;
   if (tid < K) {
-    const size_t zi = ((size_t)b * (L + 1) + t) * V + cl.e.cidx[tid];
+    const size_t zi = ((size_t)b * (L + 1) + t) * V + cidx_l;
     zv = DT == DFLASH_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Z)[zi] << 16)
                            : reinterpret_cast<const float*>(Z)[zi];
   }
-  const float sv = edge_contract<PT>(cl.e, E, K, r, S + (size_t)bt * K * K);
+  const float sv = edge_contract_rows<PT>(cl.e, E, K, r, pl, cidx_l, cl_j, S + (size_t)bt * K * K);
   if (tid < K) zc[(size_t)bt * K + tid] = zv;
   // S4's table rows (t, i) of this edge: the walk's decision and q from
   // every predecessor rank i (thread tid holds S[tid / 16][tid % 16])

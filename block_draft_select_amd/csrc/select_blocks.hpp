@@ -192,9 +192,10 @@ struct Run {
   }
 };
 
-// Scores of one edge from the staged lists in `e` (pidx, cidx, cl and g
-// filled, barrier passed):
-// S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k].
+// Scores of one edge, S[i][j] = cl[j] + sum_k E[pidx_i,k] g_t[k] E[cidx_j,k],
+// with g_t staged in e.g (barrier passed) and, in registers, this lane's
+// operand tokens (pidx_l = pidx_{l%16}, cidx_l = cidx_{l%16}) and this
+// thread's candidate logit (cl_j = cl[tid % 16]).
 // The 16 x r x 16 contraction runs on the matrix cores in fp32
 // (v_mfma_f32_16x16x4_f32) with operands taken straight from the gathered
 // embedding rows: wave w covers k in [w r/4, (w+1) r/4); lane group
@@ -209,14 +210,14 @@ struct Run {
 // where both indices are below K), so wave w holds rows 4 w .. 4 w + 3, one
 // per 16-lane group.
 template <int PT>
-__device__ __forceinline__ float edge_contract(EdgeLds& e, const void* __restrict__ E, int K, int r,
-                                               float* __restrict__ S_edge) {
+__device__ __forceinline__ float edge_contract_rows(EdgeLds& e, const void* __restrict__ E, int K, int r, int pidx_l,
+                                                    int cidx_l, float cl_j, float* __restrict__ S_edge) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = r >> 4;
   const int k0 = ((wave << 2) + (lane >> 4)) * n;
   Run<PT> av, cv;
-  av.load(E, e.pidx[lane & 15], r, k0, n);
-  cv.load(E, e.cidx[lane & 15], r, k0, n);
+  av.load(E, pidx_l, r, k0, n);
+  cv.load(E, cidx_l, r, k0, n);
   v4f32 acc = (v4f32){0.f, 0.f, 0.f, 0.f};
   if (n == 16) {  // r = 256: straight-line steps
 #pragma unroll
@@ -233,9 +234,18 @@ __device__ __forceinline__ float edge_contract(EdgeLds& e, const void* __restric
   const int i = tid >> 4, j = tid & 15;
   const int ln = ((i >> 2) << 4) + j, v = i & 3;
   const float d = ((e.red[0][v][ln] + e.red[1][v][ln]) + e.red[2][v][ln]) + e.red[3][v][ln];
-  const float sv = e.cl[j] + d;
+  const float sv = cl_j + d;
   if (i < K && j < K) S_edge[i * K + j] = sv;
   return sv;
+}
+
+// The same with the tokens and logits taken from the lists staged in `e`
+// (pidx, cidx, cl and g filled, barrier passed).
+template <int PT>
+__device__ __forceinline__ float edge_contract(EdgeLds& e, const void* __restrict__ E, int K, int r,
+                                               float* __restrict__ S_edge) {
+  const int lane = threadIdx.x & 63;
+  return edge_contract_rows<PT>(e, E, K, r, e.pidx[lane & 15], e.cidx[lane & 15], e.cl[threadIdx.x & 15], S_edge);
 }
 
 // ---------------------------------------------------------------- trace step
