@@ -137,9 +137,11 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
   // every thread reads the merged lists itself (no second hand-off):
   // the tokens of row lane % 16 (its MFMA operands) and the logit of
   // candidate tid % 16 (its score's column)
+  // (clamped: a row with fewer than K admissible values leaves empty list
+  // slots, whose key decodes to -1; the gathers below must stay in range)
   const int rl = tid & 15;
-  const int pl = rl < K ? (t == 0 ? clamp_idx(x0[b], V) : key_index(cl.prev[rl])) : (t == 0 ? clamp_idx(x0[b], V) : -1);
-  const int cidx_l = rl < K ? key_index(cl.cur[rl]) : -1;
+  const int pl = rl < K ? clamp_idx(t == 0 ? x0[b] : key_index(cl.prev[rl]), V) : (t == 0 ? clamp_idx(x0[b], V) : -1);
+  const int cidx_l = rl < K ? clamp_idx(key_index(cl.cur[rl]), V) : -1;
   const float cl_j = rl < K ? key_value(cl.cur[rl]) : 0.f;
   if (tid < K) {
     const size_t o = (size_t)bt * K + tid;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void topk_output_kernel(const uint64_t* __rest
   const int row = blockIdx.x, tid = threadIdx.x;
   merge_row(partial + (size_t)row * n_seg * 16, n_seg, K, keys, out);
   if (tid < K) {
-    cand_idx[(size_t)row * K + tid] = key_index(out[tid]);
+    cand_idx[(size_t)row * K + tid] = key_index(out[tid]);  // -1: an empty slot (no admissible value)
     cand_logit[(size_t)row * K + tid] = key_value(out[tid]);
   }
 }

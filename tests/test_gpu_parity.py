@@ -112,6 +112,23 @@ def test_extreme_shapes(name, cid, kw, streams):
         compare_stream(gpu, ref[b], b)
 
 
+def test_rows_without_admissible_values_stay_in_range():
+    # a drafter row made only of the all-ones NaN pattern has no admissible
+    # value, so its top lists stay empty; the cycle must still keep every
+    # index it gathers and writes in range (the other stream is unaffected)
+    inp = synth.make(3, set_id=6, B=2, V=8192, hidden=256)
+    _say("[parity] empty candidate lists")
+    ref, _ = guarded(inp, streams=[0])
+    inp["U"][1] = 0xFFFF
+    gpu = run_cycle(inp)
+    compare_stream(gpu, ref[0], 0)
+    V, L = inp["V"], inp["L"]
+    assert np.all((gpu["cand_idx"][1] >= 0) & (gpu["cand_idx"][1] < V))
+    assert 0 <= gpu["accept_len"][1] <= L
+    assert np.all((gpu["out_tok"][1] >= -1) & (gpu["out_tok"][1] < V))
+    assert np.all((gpu["path_rank"][1] >= 0) & (gpu["path_rank"][1] < inp["K"]))
+
+
 def test_split_entry_points_equal_cycle():
     import torch
     import block_draft_select_amd as dfl
