@@ -89,24 +89,19 @@ __device__ void merge_buffer(TkWave& w, uint32_t cnt, int K, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     if (lane < (int)c && rank < (uint32_t)K) w.top[rank] = mine;
   } else {
-    constexpr int SL = (kTopkCap + 16) / kWave + 1;
-    uint64_t mine[SL];
-    uint32_t rank[SL];
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const uint32_t i = lane + s * kWave;
-      mine[s] = i < c ? w.buf[i] : 0ull;
-      rank[s] = i < ntop ? i : (i < c ? (uint32_t)count_greater(w.buf, (int)ntop, mine[s]) : 0xFFFFu);
-    }
-    for (uint32_t j = ntop; j < c; ++j) {
-      const uint64_t o = w.buf[j];
-#pragma unroll
-      for (int s = 0; s < SL; ++s) rank[s] += (o > mine[s]) ? 1u : 0u;
+    // rare (more than one key per lane): one slot of 64 keys at a time,
+    // not unrolled, so that this path does not set the register count of
+    // every launch that inlines it; ranks come from buf only, so each
+    // slot's keys can be placed before the next slot is ranked
+#pragma unroll 1
+    for (uint32_t s0 = 0; s0 < c; s0 += kWave) {
+      const uint32_t i = s0 + lane;
+      const uint64_t mine = i < c ? w.buf[i] : 0ull;
+      uint32_t rank = i < ntop ? i : (i < c ? (uint32_t)count_greater(w.buf, (int)ntop, mine) : 0xFFFFu);
+      for (uint32_t j = ntop; j < c; ++j) rank += (w.buf[j] > mine) ? 1u : 0u;
+      if (mine != 0ull && rank < (uint32_t)K) w.top[rank] = mine;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-    for (int s = 0; s < SL; ++s)
-      if (mine[s] != 0ull && rank[s] < (uint32_t)K) w.top[rank[s]] = mine[s];
   }
   if (lane == 0) w.ntop = min(c, (uint32_t)K);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -120,8 +115,10 @@ __device__ __forceinline__ int slot_index_bf16(int lo, int lane, int s) {
 
 // Exact top-K of one sub-segment whose threshold admits too many values
 // (long runs of equal values).  Re-reads the sub-segment on every bisection
-// step, so the hot path keeps no extra registers; appends K keys to the
-// buffer after its first `base` entries.
+// step, one slot at a time (the slot loops stay rolled: unrolled, the
+// compiler hoists every slot's load out of the bisection and this rare path
+// would set the register count of the launches that call it); appends K
+// keys to the buffer after its first `base` entries.
 template <int DT>
 __device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int hi, int K, int lane,
                                               TkWave& w, uint32_t base) {
@@ -145,6 +142,7 @@ __device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int h
   for (int bit = VBITS - 1; bit >= 0; --bit) {
     const uint32_t c = tv | (1u << bit);
     uint32_t n = 0;
+#pragma unroll 1
     for (int s = 0; s < NS; ++s) {
       int idx;
       n += (cv(s, idx) >= c) ? 1u : 0u;
@@ -152,6 +150,7 @@ __device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int h
     if (wave_sum_u32(n) >= (uint32_t)K) tv = c;
   }
   uint32_t gt = 0;
+#pragma unroll 1
   for (int s = 0; s < NS; ++s) {
     int idx;
     gt += (cv(s, idx) > tv) ? 1u : 0u;
@@ -163,6 +162,7 @@ __device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int h
   while (xlo < xhi) {
     const int mid = (xlo + xhi) >> 1;
     uint32_t n = 0;
+#pragma unroll 1
     for (int s = 0; s < NS; ++s) {
       int idx;
       n += (cv(s, idx) == tv && idx <= mid) ? 1u : 0u;
@@ -171,6 +171,7 @@ __device__ __noinline__ void exact_subsegment(const void* row_ptr, int lo, int h
   }
   if (lane == 0) w.cnt = base;
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll 1
   for (int s = 0; s < NS; ++s) {
     int idx;
     const uint32_t v = cv(s, idx);
