@@ -206,12 +206,77 @@ __device__ __forceinline__ void append_hits(bool hit, uint64_t key, TkWave& w, u
   cnt += (uint32_t)__popcll(b);
 }
 
-// append both bf16 values of one register whose 16-bit ordered key >= thr
-__device__ __forceinline__ void append_pair(uint32_t raw, int idx0, uint32_t thr, TkWave& w, uint32_t& cnt) {
-  const uint32_t k2 = ord16x2(raw);
-  const uint32_t klo = k2 & 0xFFFFu, khi = k2 >> 16;
-  append_hits(klo >= thr, make_key(ord32_of_k16(klo), (uint32_t)idx0), w, cnt);
-  append_hits(khi >= thr, make_key(ord32_of_k16(khi), (uint32_t)(idx0 + 1)), w, cnt);
+// bf16 candidates are buffered as 32-bit compact keys: the 16-bit ordered
+// key (-0.0 folded onto +0.0) in the high half, 0xFFFE minus the value's
+// offset in its sub-segment (< 4096) in the low half.  Within a sub-segment
+// the compact order is the key order (value desc, index asc).  A running
+// key (from an earlier sub-segment, so a smaller index) is written as its
+// 16-bit head with low half 0xFFFF: it beats every compact key of equal
+// value and no compact key equals it.
+
+// Append the hits of one register (its low and high bf16 value) as compact
+// keys after the first `cnt` entries of cb.  cnt is wave-uniform; a lane's
+// slot is the number of hitting lanes below it.  Past the capacity nothing
+// is written but cnt still counts, which sends the fold to the exact path.
+__device__ __forceinline__ void append2_compact(bool hlo, bool hhi, uint32_t key_lo, uint32_t key_hi,
+                                                uint32_t* cb, uint32_t& cnt) {
+  const uint64_t blo = __ballot(hlo), bhi = __ballot(hhi);
+  const uint32_t nlo = (uint32_t)__popcll(blo);
+  const uint32_t n = nlo + (uint32_t)__popcll(bhi);
+  if (cnt + n <= (uint32_t)kTopkCap) {
+    if (hlo) cb[cnt + lanes_below(blo)] = key_lo;
+    if (hhi) cb[cnt + nlo + lanes_below(bhi)] = key_hi;
+  }
+  cnt += n;
+}
+
+// Merge the compact buffer cb[0, c) (running heads, then new keys) into the
+// running list; lo is the sub-segment's first index.  c > kWave (rare)
+// widens the keys into the 64-bit buffer and takes the general merge.
+__device__ void merge_compact_bf16(TkWave& w, uint32_t c, int K, int lane, int lo) {
+  const uint32_t ntop = w.ntop;
+  if (c == ntop) return;  // nothing new
+  const uint32_t* cb = reinterpret_cast<const uint32_t*>(w.buf);
+  auto widen = [&](uint32_t ck) -> uint64_t {
+    return make_key(ord32_of_k16(ck >> 16), (uint32_t)lo + (0xFFFEu - (ck & 0xFFFFu)));
+  };
+  if (c <= (uint32_t)kWave) {
+    const uint32_t mine = lane < (int)c ? cb[lane] : 0u;
+    const uint64_t run = lane < (int)ntop ? w.top[lane] : 0ull;
+    // a running key counts only the new keys above it (running heads of
+    // equal value must not count each other); a new key counts all
+    const uint32_t j_first = lane < (int)ntop ? ntop : 0u;
+    uint32_t rank = lane < (int)ntop ? (uint32_t)lane : 0u;
+    for (uint32_t j0 = 0; j0 < c; j0 += 16) {
+      uint32_t o[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) o[u] = cb[j0 + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) rank += (j0 + u >= j_first && j0 + u < c && o[u] > mine) ? 1u : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < (int)c && rank < (uint32_t)K) w.top[rank] = lane < (int)ntop ? run : widen(mine);
+    if (lane == 0) w.ntop = min(c, (uint32_t)K);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  } else {
+    // every lane reads its (up to kTopkCap / kWave) keys before any lane
+    // writes the widened ones over the same LDS
+    constexpr int SL = kTopkCap / kWave;
+    uint32_t ck[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint32_t i = lane + s * kWave;
+      ck[s] = i < c ? cb[i] : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint32_t i = lane + s * kWave;
+      if (i < c) w.buf[i] = i < ntop ? w.top[i] : widen(ck[s]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    merge_buffer(w, c, K, lane);
+  }
 }
 
 // Fold bf16 sub-segment [lo, hi) of `row` into the wave's running list.
@@ -219,14 +284,20 @@ __device__ __forceinline__ void append_pair(uint32_t raw, int idx0, uint32_t thr
 // actual value per lane (the lane maximum whenever the lane holds a
 // non-negative value); the K-th largest of those picks is a valid
 // threshold.  When the threshold is positive, a raw pattern passes exactly
-// when it is >= the threshold's pattern as a signed 16-bit integer, so the
-// candidate test needs no key transform.
-__device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w, int lane,
-                               uint32_t* bbound) {
+// when it is >= the threshold's pattern as a signed 16-bit integer, and
+// its ordered key is the pattern with the sign bit set, so neither the test
+// nor the compact key needs a key transform.
+//
+// The fold runs in two steps so that a block can share its first
+// thresholds before any wave scans: fold_bf16_load fills the registers and
+// returns the wave's own threshold key (the running list's K-th key + 1, or
+// the K-th largest pick); fold_bf16_scan raises it to the block bound, then
+// buffers and merges the candidates.
+__device__ __forceinline__ uint32_t fold_bf16_load(const uint16_t* __restrict__ row, int lo, int hi, int K,
+                                                   const TkWave& w, int lane, uint32_t (&x)[4 * kTopkLoads]) {
   // 16-byte units lie wholly inside or outside [lo, hi) (row lengths are
   // multiples of 8 values); units past hi hold 0xFFFF pairs (key 0: never
   // admitted, and a lane whose pick is padding adds nothing to the count)
-  uint32_t x[4 * kTopkLoads];
 #pragma unroll
   for (int j = 0; j < kTopkLoads; ++j) {
     const int base = lo + (j * kWave + lane) * 8;
@@ -237,7 +308,7 @@ __device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi,
     x[4 * j + 2] = v.z;
     x[4 * j + 3] = v.w;
   }
-  const uint32_t ntop = w.ntop;
+  const uint32_t ntop = __builtin_amdgcn_readfirstlane(w.ntop);
   uint32_t thr;
   if (ntop == (uint32_t)K) {
     thr = (uint32_t)(w.top[K - 1] >> 48) + 1u;
@@ -256,33 +327,65 @@ __device__ void wave_fold_bf16(const uint16_t* __restrict__ row, int lo, int hi,
     if (thr == 0x8000u) thr = 0x7FFFu;  // a +0.0 threshold also admits -0.0
     if (thr == 0u) thr = 1u;            // never admit padding
   }
+  return thr;
+}
+
+__device__ __forceinline__ void fold_bf16_scan(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w,
+                                               int lane, uint32_t* bbound, const uint32_t (&x)[4 * kTopkLoads],
+                                               uint32_t thr) {
+  const uint32_t ntop = __builtin_amdgcn_readfirstlane(w.ntop);
   uint32_t sb = *bbound;                // 16-bit key of the block bound
   if (sb == 0x8000u) sb = 0x7FFFu;      // a +0.0 bound also admits -0.0
-  thr = max(thr, sb);
+  thr = __builtin_amdgcn_readfirstlane(max(thr, sb));
 
-  // buffer = running list, then the new candidates; a register is looked
-  // at closely only when some lane's register passes the packed test
-  if (lane < (int)ntop) w.buf[lane] = w.top[lane];
+  // compact buffer = running heads, then the new candidates; a register is
+  // looked at closely only when some lane's register passes the packed test
+  uint32_t* cb = reinterpret_cast<uint32_t*>(w.buf);
+  if (lane < (int)ntop) cb[lane] = ((uint32_t)(w.top[lane] >> 48) << 16) | 0xFFFFu;
   uint32_t cnt = ntop;
+  // low half of the compact key of the lane's first value in each register
+  // group: 0xFFFE - lane * 8, minus the register's constant offset below.
+  // Opaque to the optimiser: otherwise the 32 per-register values are
+  // hoisted out of the caller's sub-segment loop and held in registers
+  uint32_t lane_lo = 0xFFFEu - (uint32_t)lane * 8u;
+  asm volatile("" : "+v"(lane_lo));
   if (thr > 0x8000u && thr <= 0xFFFFu) {
-    const uint32_t tm1 = ((thr & 0x7FFFu) - 1u) * 0x00010001u;  // positive pattern - 1, both halves
+    const int tp = (int)(thr & 0x7FFFu);  // positive threshold pattern
+    const uint32_t tm1 = (uint32_t)(tp - 1) * 0x00010001u;
+    const uint32_t pos_lo = 0x80000000u | lane_lo;  // sign bit of a positive key
 #pragma unroll
-    for (int q = 0; q < 4 * kTopkLoads; ++q)
-      if (__ballot(max_i16x2(x[q], tm1) != tm1))
-        append_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w, cnt);
+    for (int q = 0; q < 4 * kTopkLoads; ++q) {
+      if (__ballot(max_i16x2(x[q], tm1) != tm1)) {
+        const uint32_t low = pos_lo - (uint32_t)((q >> 2) * kWave * 8 + (q & 3) * 2);
+        append2_compact((int)(int16_t)(x[q] & 0xFFFFu) >= tp, (int)x[q] >> 16 >= tp, (x[q] << 16) | low,
+                        (x[q] & 0xFFFF0000u) | (low - 1u), cb, cnt);
+      }
+    }
   } else if (thr <= 0xFFFFu) {
     const uint32_t tm1 = (thr - 1u) * 0x00010001u;
 #pragma unroll
-    for (int q = 0; q < 4 * kTopkLoads; ++q)
-      if (__ballot(subsat_u16x2(ord16x2(x[q]), tm1) != 0u))
-        append_pair(x[q], lo + ((q >> 2) * kWave + lane) * 8 + (q & 3) * 2, thr, w, cnt);
+    for (int q = 0; q < 4 * kTopkLoads; ++q) {
+      const uint32_t k2 = ord16x2(x[q]);
+      if (__ballot(subsat_u16x2(k2, tm1) != 0u)) {
+        uint32_t klo = k2 & 0xFFFFu, khi = k2 >> 16;
+        klo = klo == 0x7FFFu ? 0x8000u : klo;
+        khi = khi == 0x7FFFu ? 0x8000u : khi;
+        const uint32_t low = lane_lo - (uint32_t)((q >> 2) * kWave * 8 + (q & 3) * 2);
+        append2_compact(klo >= thr, khi >= thr, (klo << 16) | low, (khi << 16) | (low - 1u), cb, cnt);
+      }
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   if (cnt > (uint32_t)kTopkCap) {
+    // too many candidates: the 64-bit buffer gets the running list back and
+    // the exact path appends the sub-segment's own top K
+    if (lane < (int)ntop) w.buf[lane] = w.top[lane];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     exact_subsegment<DFLASH_BF16>(row, lo, hi, K, lane, w, ntop);
-    cnt = w.cnt;
+    merge_buffer(w, w.cnt, K, lane);
+  } else {
+    merge_compact_bf16(w, cnt, K, lane, lo);
   }
-  merge_buffer(w, cnt, K, lane);
   if (lane == 0 && w.ntop == (uint32_t)K) atomicMax(bbound, (uint32_t)(w.top[K - 1] >> 48));
 }
 
@@ -364,12 +467,30 @@ __device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, in
   if (tid == 0) *bbound = 0u;
   __syncthreads();
   const int s1 = min((seg + 1) * spb, n_sub);
-  for (int s = seg * spb + wave; s < s1; s += 4) {
-    const int lo = s * WS, hi = min(lo + WS, V);
-    if (DT == DFLASH_BF16)
-      wave_fold_bf16(reinterpret_cast<const uint16_t*>(U) + (size_t)row * V, lo, hi, K, w, lane, bbound);
-    else
+  if (DT == DFLASH_BF16) {
+    // first sub-segments: every wave publishes its own threshold before any
+    // wave scans, so each scans against the largest of the four (any wave's
+    // K-th largest pick bounds the block's K-th value from below)
+    const uint16_t* rp = reinterpret_cast<const uint16_t*>(U) + (size_t)row * V;
+    uint32_t x[4 * kTopkLoads];
+    const int s0 = seg * spb + wave;
+    uint32_t thr = 0;
+    if (s0 < s1) {
+      thr = fold_bf16_load(rp, s0 * WS, min(s0 * WS + WS, V), K, w, lane, x);
+      if (lane == 0) atomicMax(bbound, thr);
+    }
+    __syncthreads();
+    if (s0 < s1) fold_bf16_scan(rp, s0 * WS, min(s0 * WS + WS, V), K, w, lane, bbound, x, thr);
+    for (int s = s0 + 4; s < s1; s += 4) {
+      const int lo = s * WS, hi = min(lo + WS, V);
+      thr = fold_bf16_load(rp, lo, hi, K, w, lane, x);
+      fold_bf16_scan(rp, lo, hi, K, w, lane, bbound, x, thr);
+    }
+  } else {
+    for (int s = seg * spb + wave; s < s1; s += 4) {
+      const int lo = s * WS, hi = min(lo + WS, V);
       wave_fold_f32(reinterpret_cast<const uint32_t*>(U) + (size_t)row * V, lo, hi, K, w, lane, bbound);
+    }
   }
   if (tid < 16) block_top[tid] = 0ull;
   __syncthreads();

@@ -173,7 +173,7 @@ def test_topk_alone_special_rows():
     import block_draft_select_amd as dfl
     from oracle import dflash as O
     _say("[parity] topk special rows")
-    V, K, L = 16392, 16, 6
+    V, K, L = 16392, 16, 8
     rng = np.random.default_rng(3)
     rows = np.zeros((L, V), dtype=np.float32)
     rows[0] = 1.5                                           # all equal: lowest 16 indices
@@ -184,6 +184,14 @@ def test_topk_alone_special_rows():
     rows[3] = np.sort(rng.standard_normal(V))               # ascending: top at the ragged tail
     rows[4] = np.round(rng.standard_normal(V) * 2) / 2      # heavy ties
     rows[5] = rng.standard_normal(V) * 1e-3 - 50.0           # all negative
+    # equal maxima scattered through every 4096-value block: about 100 per
+    # block (more candidates than one per lane) and about 300 (more than
+    # the candidate buffer holds)
+    for t_, n_ in ((6, 100), (7, 300)):
+        rows[t_] = -1.0
+        for b0 in range(0, V, 4096):
+            pos = rng.choice(np.arange(b0, min(b0 + 4096, V)), size=min(n_, V - b0), replace=False)
+            rows[t_, pos] = 2.0
     bits = synth.bf16_bits(rows)
     inp = dict(B=1, L=L, V=V, K=K, r=16, hidden=16, logit_kind="bf16", param_kind="bf16")
     d = dims_of(inp)
