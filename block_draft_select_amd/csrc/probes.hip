@@ -1,5 +1,6 @@
-// Workspace fill and the two measurement kernels (plain streaming read and
-// plain copy) used to calibrate bandwidth figures and hardware counters.
+// Workspace fill and the two measurement kernels (one-pass nontemporal
+// streaming read and plain copy) used to calibrate bandwidth figures and
+// hardware counters.
 #include "device_util.hpp"
 #include "internal.hpp"
 
@@ -14,23 +15,25 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, s
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+// One pass: each wave reads one contiguous 8 KB piece with eight 16-byte
+// nontemporal loads per lane, all issued before the first is used (the
+// access shape of the streaming launch's waves, without their arithmetic).
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
                                                          uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t base = (size_t)blockIdx.x * 2048 + (threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
+  uint4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const size_t i = base + (size_t)j * 64;
+    v[j] = i < n16 ? load_stream16(p + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
   uint32_t acc = 0;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
-  }
-  for (; i < n16; i += stride) {
-    const uint4 a = p[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   // The store depends on every loaded word, so no load can be dropped, but
   // it happens (practically) never: a per-wave atomic would serialise the
   // waves on one address and measure the atomic unit instead of HBM.
-  if (acc == 0x9E3779B9u) sink[0] = acc ^ (uint32_t)i;
+  if (acc == 0x9E3779B9u) sink[0] = acc ^ (uint32_t)base;
 }
 
 __global__ __launch_bounds__(256) void copy_probe_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
@@ -56,8 +59,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
   const size_t n16 = bytes / 16;
-  launch(read_probe_kernel, dim3(grid_for(n16)), dim3(256), st,
-                     reinterpret_cast<const uint4*>(buf), n16, sink);
+  const size_t blocks = (n16 + 2047) / 2048;  // 32 KB per block
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  launch(read_probe_kernel, dim3((unsigned)blocks), dim3(256), st, reinterpret_cast<const uint4*>(buf), n16,
+         sink);
   return hipGetLastError();
 }
 

@@ -183,10 +183,12 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
 
 /* ---- measurement helpers (not part of the method) ---------------------- */
 
-/* Stream-read `bytes` (multiple of 16, 16-byte aligned) of `buf`: the
- * achievable HBM read ceiling.  Each lane folds its words with XOR and
- * stores to *sink only if the fold equals one fixed constant, so the loads
- * cannot be elided; *sink is normally left untouched. */
+/* Stream-read `bytes` (multiple of 16, 16-byte aligned) of `buf` once: the
+ * achievable HBM read ceiling for the streaming launch's access shape (each
+ * wave one contiguous 8 KB piece, nontemporal 16-byte loads, all in flight
+ * together).  Each lane folds its words with XOR and stores to *sink only if
+ * the fold equals one fixed constant, so the loads cannot be elided; *sink
+ * is normally left untouched. */
 dflash_status dflash_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Plain copy of `bytes` (multiple of 16, both 16-byte aligned): the
