@@ -96,7 +96,7 @@ struct CandLds {
   uint64_t prev[16], cur[16];
 };
 
-template <int DT, int PT>
+template <int DT, int PT, bool WIDE>
 __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __restrict__ partial, int n_seg,
                                                           const int32_t* __restrict__ x0, const void* __restrict__ E,
                                                           const float* __restrict__ gpart, int n_ks,
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
   for (int q = 0; q < KPT; ++q)
     if (tid + q * 256 < 2 * nk) cl.keys[tid + q * 256] = kv[q];
   __syncthreads();
-  merge_two_staged(cl.keys, n_seg, K, cl.prev, cl.cur);
+  merge_two_staged<WIDE>(cl.keys, n_seg, K, cl.prev, cl.cur);
   // every thread reads the merged lists itself (no second hand-off):
   // the tokens of row lane % 16 (its MFMA operands) and the logit of
   // candidate tid % 16 (its score's column)
@@ -215,15 +215,21 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
   float* zc = reinterpret_cast<float*>(ws + w.zc);
   int32_t* jstar = reinterpret_cast<int32_t*>(ws + w.jstar);
   float* qtab = reinterpret_cast<float*>(ws + w.qtab);
-#define DF_SCORES(DT, PT)                                                                                      \
-  launch((cand_scores_kernel<DT, PT>), grid, dim3(256), st, partial, w.n_seg, x0, E, g, gate_groups(d), Z, d.L, \
-         d.V, d.K, d.r, T, seed, cycle, cand_idx, cand_logit, zc, S, jstar, qtab)
+#define DF_SCORES_W(DT, PT, WIDE)                                                                           \
+  launch((cand_scores_kernel<DT, PT, WIDE>), grid, dim3(256), st, partial, w.n_seg, x0, E, g, gate_groups(d), Z, \
+         d.L, d.V, d.K, d.r, T, seed, cycle, cand_idx, cand_logit, zc, S, jstar, qtab)
+#define DF_SCORES(DT, PT)                                                \
+  do {                                                                   \
+    if (merge_wide(w.n_seg)) DF_SCORES_W(DT, PT, true);                  \
+    else DF_SCORES_W(DT, PT, false);                                     \
+  } while (0)
   if (d.logit_dtype == DFLASH_BF16) {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_BF16, DFLASH_BF16); else DF_SCORES(DFLASH_BF16, DFLASH_F32);
   } else {
     if (d.param_dtype == DFLASH_BF16) DF_SCORES(DFLASH_F32, DFLASH_BF16); else DF_SCORES(DFLASH_F32, DFLASH_F32);
   }
 #undef DF_SCORES
+#undef DF_SCORES_W
   return hipGetLastError();
 }
 

@@ -538,8 +538,15 @@ __device__ __forceinline__ void merge_row(const uint64_t* __restrict__ lists, in
 // pass: each key's rank is its position in its own list plus the count of
 // greater keys in the row's other lists.  Every thread of the block takes
 // part; ends with a barrier.
+// The other lists are searched G at a time (G = 8, or 16 when a row has
+// more than 8 lists: merge_wide), each group's searches advanced level by
+// level so that a level's G loads are in flight together.
+__host__ __device__ constexpr bool merge_wide(int n_seg) { return n_seg > 8; }
+
+template <bool WIDE>
 __device__ __forceinline__ void merge_two_staged(const uint64_t* keys, int n_seg, int K, uint64_t* out0,
                                                  uint64_t* out1) {
+  constexpr int G = WIDE ? 16 : 8;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int nk = n_seg * 16;
   for (int i = tid; i < 2 * nk; i += nt) {
@@ -548,27 +555,25 @@ __device__ __forceinline__ void merge_two_staged(const uint64_t* keys, int n_seg
     const uint64_t key = keys[i];
     if (key == 0ull || k >= K) continue;
     const uint64_t* base = keys + half * nk;
-    // the other lists' counts: eight binary searches at a time, level by
-    // level, so each level's eight loads are in flight together
     int rank = k;
-    for (int g0 = 0; g0 < n_seg; g0 += 8) {
-      const uint64_t* lp[8];
-      int lo[8];
-      bool l15[8];
+    for (int g0 = 0; g0 < n_seg; g0 += G) {
+      const uint64_t* lp[G];
+      int lo[G];
+      bool l15[G];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < G; ++q) {
         lp[q] = base + min(g0 + q, n_seg - 1) * 16;
         l15[q] = lp[q][15] > key;
         lo[q] = lp[q][7] > key ? 8 : 0;
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q] + 3] > key ? 4 : 0;
+      for (int q = 0; q < G; ++q) lo[q] += lp[q][lo[q] + 3] > key ? 4 : 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q] + 1] > key ? 2 : 0;
+      for (int q = 0; q < G; ++q) lo[q] += lp[q][lo[q] + 1] > key ? 2 : 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) lo[q] += lp[q][lo[q]] > key ? 1 : 0;
+      for (int q = 0; q < G; ++q) lo[q] += lp[q][lo[q]] > key ? 1 : 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < G; ++q) {
         const int s2 = g0 + q;
         if (s2 < n_seg && s2 != s) rank += lo[q] == 15 && l15[q] ? 16 : lo[q];
       }

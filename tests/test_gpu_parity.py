@@ -98,6 +98,9 @@ EXTREME = [
     ("bf16-V-eq-K", 3, dict(B=3, V=16, K=16, hidden=256, plant=None), None),
     ("f32-V-eq-K4", 1, dict(B=2, V=4, K=4, T=0.8), None),
     ("bf16-max-V", 3, dict(B=1, L=4, V=2097152, hidden=256, plant=None), None),
+    # one stream of a 151936-token vocabulary: ten partial lists per row
+    ("bf16-ten-lists-T0", 2, dict(B=1, V=151936, hidden=256), None),
+    ("bf16-ten-lists-T1", 3, dict(B=1, V=151936, hidden=256), None),
     ("bf16-max-rows", 3, dict(B=3855, L=16, V=64, hidden=16, r=16, plant=None), [0, 1, 1927, 3854]),
 ]
 
