@@ -14,14 +14,16 @@
 //      (plus one: later indices lose ties) is a second lower bound; the
 //      larger one is the threshold;
 //   2. values at or above the threshold are appended to an LDS buffer next
-//      to the running list and merged into it by exact rank (value desc,
-//      index asc).
+//      to the running list (bf16: as 32-bit compact keys, widened to the
+//      64-bit list keys only when they enter the list) and merged into it
+//      by exact rank (value desc, index asc).
 // Once a wave's running list is full, its K-th key + 1 replaces the
 // per-sub-segment threshold (later sub-segments have larger indices and
 // lose ties), and the bisection is skipped.  The four waves of a block also
-// share a lower bound in LDS: any wave's K-th value bounds the block's K-th
-// value from below, so smaller values cannot be in the block's list (equal
-// values still can, by index).
+// share a lower bound in LDS: any wave's K-th largest pick, and later any
+// wave's K-th list value, bounds the block's K-th value from below, so
+// smaller values cannot be in the block's list (equal values still can, by
+// index).  For bf16 the first thresholds are shared before any wave scans.
 // A tie-heavy sub-segment whose candidates overflow the buffer takes an
 // out-of-line exact path that re-reads it.  A block (4 waves) owns a run of
 // sub-segments and writes the sorted top list of that run; the lists of a
