@@ -14,6 +14,8 @@ that a reader can check each step against the pages by eye:
 * ``oracle.dflash``  -- top-K candidate extraction, the context gate, adjacent
   pair scores, the lattice trace, the rejection-sampling verify, and the
   decision margins the input guard uses.
+* ``oracle.conv``    -- the two-tap dynamic depthwise convolution of the
+  drafter's block representations.
 
 Pinned by ``tests/test_oracle_*.py`` against known-answer vectors, closed
 forms, brute-force enumeration and chi-square tests (see each function's
@@ -24,3 +26,4 @@ documented in ``oracle.dflash.pair_scores`` fixes them.
 
 from . import philox  # noqa: F401
 from . import dflash  # noqa: F401
+from . import conv  # noqa: F401

@@ -181,3 +181,22 @@ def make(config_id, set_id=0, *, B=None, L=None, V=None, K=None, r=None,
                 U=U, Z=Z, x0=x0, E=E, W=W, h=h, T=Tb.astype(np.float32), seed=seed,
                 cycle=int(set_id if cycle is None else cycle),
                 planted=planted, planted_rank=planted_rank)
+
+
+def make_conv(config_id, set_id=0, *, B=None, L=None, hidden=None, kind=None, w_std=0.02):
+    """Inputs of the two-tap convolution for configuration ``config_id``:
+    the block representations x [B, L, hidden] and their first predecessor
+    x0 [B, hidden] (standard normal, like the gate's context vectors), and
+    the tap generator Wt [2 * hidden, hidden] (normal, ``w_std``), stored in
+    the configuration's parameter kind unless ``kind`` overrides it."""
+    cfg = dict(CONFIGS[config_id])
+    Bn = int(B if B is not None else cfg["B"])
+    Ln = int(L if L is not None else cfg["L"])
+    Hn = int(hidden if hidden is not None else cfg["hidden"])
+    pk = kind or cfg["param_kind"]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([config_id, set_id, 77])))
+    x = _store(rng.standard_normal((Bn, Ln, Hn), dtype=np.float32), pk)
+    x0 = _store(rng.standard_normal((Bn, Hn), dtype=np.float32), pk)
+    Wt = _store(rng.standard_normal((2 * Hn, Hn), dtype=np.float32) * np.float32(w_std), pk)
+    return dict(config_id=config_id, set_id=set_id, B=Bn, L=Ln, hidden=Hn, param_kind=pk, x=x, x0=x0, Wt=Wt)
+
