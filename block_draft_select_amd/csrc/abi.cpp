@@ -345,6 +345,20 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, c
   }
 }
 
+dflash_status dflash_conv2tap(const dflash_dims* d, const void* x, const void* x0, const void* Wt, float* y,
+                              void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{x, "x", true}, {x0, "x0", false}, {Wt, "Wt", true}, {y, "y", false}})) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_CONV2TAP, st, [&] { return dfk::launch_conv2tap(*d, x, x0, Wt, y, st); }),
+                      "conv2tap launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
 dflash_status dflash_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   try {
     g_err.clear();
@@ -369,7 +383,7 @@ dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* 
 
 const char* dflash_kernel_name(int32_t kernel) {
   static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize",
-                                                   "cycle_stream", "cycle_scores", "cycle_finalize"};
+                                                   "cycle_stream", "cycle_scores", "cycle_finalize", "conv2tap"};
   return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
 }
 

@@ -99,6 +99,8 @@ hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const 
                                  const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
                                  int32_t* out_tok, hipStream_t st);
+hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, const void* Wt, float* y,
+                           hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st);

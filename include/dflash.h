@@ -183,6 +183,25 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
 
 /* ---- measurement helpers (not part of the method) ---------------------- */
 
+/* The two-tap dynamic depthwise convolution of the drafter's block
+ * representations (P1 "DFlash 2: Block diffusion, wearing a drafter's coat",
+ * "The architecture", "Suffix-decay convolution"; P2 "A 2B Drafter Made a
+ * 27B Model 3.4x Faster. Same Exact Output.", "The two fixes"):
+ *   [w0_t | w1_t] = Wt x_t,  y_t = w0_t * x_t + w1_t * x_{t-1},
+ * with x_0 = x0 (the representation of the last verified position).  The
+ * tap generator is not on the pages; this linear map is a reading.
+ *   d   uses B, L, hidden and param_dtype (the whole struct is validated)
+ *   x   [B, L, hidden]   param_dtype, 16-byte aligned
+ *   x0  [B, hidden]      param_dtype
+ *   Wt  [2*hidden, hidden] param_dtype, 16-byte aligned: row c generates
+ *       w0[c], row hidden + c generates w1[c] (k contiguous per tap)
+ *   y   [B, L, hidden]   fp32, written
+ * Caller-owned device buffers; one launch on `stream`; no workspace.  fp32
+ * accumulation (bf16 products are exact in fp32).  Invalid arguments launch
+ * nothing and leave y untouched. */
+dflash_status dflash_conv2tap(const dflash_dims* d, const void* x, const void* x0, const void* Wt, float* y,
+                              void* stream);
+
 /* Stream-read `bytes` (multiple of 16, 16-byte aligned) of `buf` once: the
  * achievable HBM read ceiling for the streaming launch's access shape (each
  * wave one contiguous 8 KB piece, nontemporal 16-byte loads, all in flight
@@ -206,7 +225,8 @@ enum {
   DFLASH_KERNEL_CYCLE_STREAM = 6,   /* dflash_cycle: gate + top-K lists + target chunk statistics */
   DFLASH_KERNEL_CYCLE_SCORES = 7,   /* dflash_cycle: candidates + pair scores */
   DFLASH_KERNEL_CYCLE_FINALIZE = 8, /* dflash_cycle: trace + verify */
-  DFLASH_KERNEL_COUNT = 9
+  DFLASH_KERNEL_CONV2TAP = 9,       /* dflash_conv2tap */
+  DFLASH_KERNEL_COUNT = 10
 };
 
 /* Name of a kernel identifier ("" if out of range). */

@@ -97,4 +97,8 @@ def test_null_and_misaligned_pointers_rejected(dfl):
     assert dfl.lib.dflash_topk(ctypes.byref(d), fake, fake, fake, fake, 16, None) == 3
     assert b"too small" in dfl.lib.dflash_last_error()
     assert dfl.lib.dflash_read_probe(fake, 17, fake, None) == 1
+    assert dfl.lib.dflash_conv2tap(ctypes.byref(d), fake, fake, None, fake, None) == 1
+    assert b"Wt is NULL" in dfl.lib.dflash_last_error()
+    assert dfl.lib.dflash_conv2tap(ctypes.byref(d), odd, fake, fake, fake, None) == 1
+    assert b"aligned" in dfl.lib.dflash_last_error()
     assert dfl.lib.dflash_profile_collect(42, None, None) == 1

@@ -1,0 +1,98 @@
+"""GPU parity of the two-tap convolution: the HIP path (``dflash_conv2tap``,
+through the C ABI) against the float64 oracle (``oracle.conv``).
+
+Bar: every output within (H + 4) * 2^-24 of its magnitude bound
+sum_k |Wt[c, k] x_t[k]| * |x_t[c]| + sum_k |Wt[H + c, k] x_t[k]| * |x_{t-1}[c]|:
+each tap is an fp32 sum of H products (exact for bf16 operands, one rounding
+each for fp32 ones), then two products and one fused add.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import _np_to_dev
+from oracle import conv as C
+from oracle import dflash as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_select_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def _run(inp):
+    import torch
+    import block_draft_select_amd as dfl
+    B, L, H, pk = inp["B"], inp["L"], inp["hidden"], inp["param_kind"]
+    d = dfl.dims(B, L, 64, 16, 16, H, "bf16", pk)
+    x, x0, Wt = (_np_to_dev(inp[k], "cuda") for k in ("x", "x0", "Wt"))
+    y = torch.full((B, L, H), float("nan"), dtype=torch.float32, device="cuda")
+    dfl.dflash_conv2tap(d, x, x0, Wt, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def _check(inp, y, streams):
+    H, pk = inp["hidden"], inp["param_kind"]
+    x = O.widen(inp["x"], pk)
+    x0 = O.widen(inp["x0"], pk)
+    Wt = O.widen(inp["Wt"], pk)
+    aW = np.abs(Wt)
+    for b in streams:
+        ref = C.conv2tap(x[b], x0[b], Wt)
+        prev = np.vstack([x0[b][None], x[b][:-1]])
+        ax = np.abs(x[b])
+        taps_mag = ax @ aW.T                                   # [L, 2H]
+        bound = taps_mag[:, :H] * ax + taps_mag[:, H:] * np.abs(prev)
+        tol = (H + 4) * 2.0 ** -24 * bound + 1e-30
+        err = np.abs(y[b] - ref)
+        bad = np.argwhere(err > tol)
+        assert bad.size == 0, (f"stream {b}: {len(bad)} outputs out of bound, first at {tuple(bad[0])}: "
+                               f"gpu {y[b][tuple(bad[0])]!r} oracle {ref[tuple(bad[0])]!r} tol {tol[tuple(bad[0])]!r}")
+
+
+CASES = [
+    # (name, config id, overrides, streams compared (None: all))
+    ("bf16-ragged", 3, dict(B=3, L=5, hidden=48), None),          # 15 rows, a half channel tile
+    ("bf16-two-row-tiles", 3, dict(B=5, L=16, hidden=272), None),  # 80 rows, 17 channel tiles
+    ("bf16-one-position", 3, dict(B=7, L=1, hidden=64), None),     # every row takes x0
+    ("f32-small", 1, dict(B=2, L=3, hidden=32), None),
+    ("f32-ragged", 1, dict(B=3, L=4, hidden=80), None),
+    ("bf16-concurrent-32", 3, dict(), None),                       # B 32, L 8, hidden 2048
+    ("bf16-large-vocab-128", 5, dict(), [0, 77, 127]),              # B 128, L 8, hidden 3072
+]
+
+
+@pytest.mark.parametrize("name,cid,kw,streams", CASES, ids=[c[0] for c in CASES])
+def test_conv2tap_matches_oracle(name, cid, kw, streams):
+    inp = synth.make_conv(cid, set_id=4, **kw)
+    _say(f"[conv] {name}: B={inp['B']} L={inp['L']} hidden={inp['hidden']} {inp['param_kind']}")
+    y = _run(inp)
+    assert np.isfinite(y).all()
+    _check(inp, y, range(inp["B"]) if streams is None else streams)
+
+
+def test_conv2tap_identity_generator_squares():
+    # current taps = x_t, previous taps = 0 (a closed form on the GPU as well):
+    # y = x * x, exact in fp32 for bf16 inputs
+    inp = synth.make_conv(3, set_id=5, B=2, L=4, hidden=96)
+    H = inp["hidden"]
+    eye = np.vstack([np.eye(H, dtype=np.float32), np.zeros((H, H), dtype=np.float32)])
+    inp["Wt"] = synth.bf16_bits(eye)
+    y = _run(inp)
+    x = O.widen(inp["x"], "bf16")
+    np.testing.assert_array_equal(y, x * x)
