@@ -109,6 +109,68 @@ def load_traffic(kernel, workload):
         return None
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense bf16 MFMA; fp32 vector (the fp32 path's VALU)
+
+
+def conv_leg(args, base, dfl):
+    """The two-tap convolution at this workload's block shape [B, L, hidden].
+
+    Generator matrices rotate across enough sets that they stream from HBM
+    rather than from the last-level cache (set 0 from the seeded generator,
+    the others drawn on the device with the same distribution).  The kernel
+    duration comes from the library's per-launch timer.  Its roofline is the
+    larger of two floors: the algorithmic bytes (x, x0 and Wt read once, y
+    written once) at 8 TB/s and the GEMM's 2 * (B*L) * hidden * (2*hidden)
+    flops at the matrix-core peak of the parameter type.
+    """
+    import torch
+    import synth
+    from gpu_util import _np_to_dev
+    B, L, H, pk = base["B"], base["L"], base["hidden"], base["param_kind"]
+    ps = 2 if pk == "bf16" else 4
+    R = B * L
+    wt_bytes = 2 * H * H * ps
+    n_sets = max(1, min(64, -(-2 * LLC_BYTES // wt_bytes)))
+    c0 = synth.make_conv(base["config_id"], set_id=0, B=B, L=L, hidden=H)
+    sets = [{k: _np_to_dev(c0[k], "cuda") for k in ("x", "x0", "Wt")}]
+    tdt = torch.bfloat16 if pk == "bf16" else torch.float32
+    for _ in range(1, n_sets):
+        sets.append({"x": torch.randn(B, L, H, device="cuda").to(tdt),
+                     "x0": torch.randn(B, H, device="cuda").to(tdt),
+                     "Wt": (torch.randn(2 * H, H, device="cuda") * 0.02).to(tdt)})
+    y = torch.empty(B, L, H, dtype=torch.float32, device="cuda")
+    d = dfl.dims(B, L, 64, 16, 16, H, "bf16", pk)
+    for i in range(max(args.warmup, n_sets)):
+        s = sets[i % n_sets]
+        dfl.dflash_conv2tap(d, s["x"], s["x0"], s["Wt"], y)
+    torch.cuda.synchronize()
+    dfl.dflash_profile_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.conv_steps):
+        s = sets[i % n_sets]
+        dfl.dflash_conv2tap(d, s["x"], s["x0"], s["Wt"], y)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / args.conv_steps
+    n, ms = dfl.dflash_profile_collect("conv2tap")
+    dfl.dflash_profile_enable(False)
+    avg_us = ms * 1e3 / n
+    nbytes = (R * H + B * H) * ps + wt_bytes + R * H * 4
+    flops = 2.0 * R * H * 2 * H
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mma = flops / (MFMA_PEAK_TFLOPS[pk] * 1e12)
+    if t_hbm >= t_mma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (avg_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(t_hbm / (avg_us * 1e-6), 4)}
+    else:
+        roof = {"bound": "mfma" if pk == "bf16" else "alu",
+                "achieved": round(flops / (avg_us * 1e-6) / 1e12, 1), "peak": MFMA_PEAK_TFLOPS[pk],
+                "unit": "TFLOP/s", "frac": round(t_mma / (avg_us * 1e-6), 4)}
+    roof.update({"algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops, "traffic": None})
+    _log(f"[bench] conv2tap {avg_us:.2f} us/launch ({roof['frac']:.2f} of its {roof['bound']} roof)")
+    return {"shape": f"B={B} L={L} hidden={H} {pk}", "launches": n, "avg_us": round(avg_us, 2),
+            "wall_us_per_call": round(wall_us, 2), "generator_sets": n_sets, "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +186,8 @@ def main():
     ap.add_argument("--read-probe", type=int, default=3,
                     help="timed passes (after one warm-up pass) of a one-pass nontemporal read over every "
                          "input set's logits (read ceiling)")
+    ap.add_argument("--conv-steps", type=int, default=200,
+                    help="timed launches of the two-tap convolution at the workload's block shape (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -232,6 +296,8 @@ def main():
             "traffic": load_traffic(dom, base["name"]), "algorithmic_bytes_per_launch": algo[dom]}
     per_kernel_roof = {k: round(algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1) for k in algo if k in kern}
 
+    conv = conv_leg(args, base, dfl) if args.conv_steps else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(base, args.cpu_seconds)
@@ -261,6 +327,7 @@ def main():
         "frac_of_read_ceiling": round(achieved / read_gbps, 4) if (read_gbps and achieved) else None,
         "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "mean_accept_len": round(mean_accept, 3),
+        "conv2tap": conv,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_sha(),
     }
