@@ -16,6 +16,8 @@ that a reader can check each step against the pages by eye:
   decision margins the input guard uses.
 * ``oracle.conv``    -- the two-tap dynamic depthwise convolution of the
   drafter's block representations.
+* ``oracle.viterbi`` -- the global max-sum path through the candidate
+  lattice (a variant of the greedy trace).
 
 Pinned by ``tests/test_oracle_*.py`` against known-answer vectors, closed
 forms, brute-force enumeration and chi-square tests (see each function's
@@ -27,3 +29,4 @@ documented in ``oracle.dflash.pair_scores`` fixes them.
 from . import philox  # noqa: F401
 from . import dflash  # noqa: F401
 from . import conv  # noqa: F401
+from . import viterbi  # noqa: F401
