@@ -171,6 +171,33 @@ def conv_leg(args, base, dfl):
             "wall_us_per_call": round(wall_us, 2), "generator_sets": n_sets, "roofline": roof}
 
 
+def viterbi_leg(args, base, dfl, dv, d, ws):
+    """The max-sum trace on input set 0's pair scores (computed once by the
+    split entry points), timed per launch with the library's timer.  It is
+    latency-bound: its bytes are the scores and candidate indices in, the
+    path, draft tokens and one-hot q out."""
+    import torch
+    from gpu_util import alloc_outputs
+    o = alloc_outputs(base)
+    dfl.dflash_topk(d, dv["U"], o["cand_idx"], o["cand_logit"], ws)
+    dfl.dflash_pair_scores(d, dv["x0"], o["cand_idx"], o["cand_logit"], dv["E"], dv["W"], dv["h"], o["S"], ws)
+    for _ in range(args.warmup):
+        dfl.dflash_trace_viterbi(d, o["S"], o["cand_idx"], o["path_rank"], o["draft_tok"], o["q"])
+    torch.cuda.synchronize()
+    dfl.dflash_profile_enable(True)
+    for _ in range(args.viterbi_steps):
+        dfl.dflash_trace_viterbi(d, o["S"], o["cand_idx"], o["path_rank"], o["draft_tok"], o["q"])
+    torch.cuda.synchronize()
+    n, ms = dfl.dflash_profile_collect("trace_viterbi")
+    dfl.dflash_profile_enable(False)
+    B, L, K = base["B"], base["L"], base["K"]
+    nbytes = B * L * K * K * 4 + B * L * K * 4 + B * L * (2 + K) * 4
+    avg_us = ms * 1e3 / n
+    _log(f"[bench] trace_viterbi {avg_us:.2f} us/launch")
+    return {"launches": n, "avg_us": round(avg_us, 2), "bytes_per_launch": nbytes, "bound": "latency",
+            "note": "one wave per stream: L dependent max-plus steps over K x K scores"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +215,8 @@ def main():
                          "input set's logits (read ceiling)")
     ap.add_argument("--conv-steps", type=int, default=200,
                     help="timed launches of the two-tap convolution at the workload's block shape (0: skip)")
+    ap.add_argument("--viterbi-steps", type=int, default=200,
+                    help="timed launches of the max-sum trace on the workload's pair scores (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -297,6 +326,7 @@ def main():
     per_kernel_roof = {k: round(algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1) for k in algo if k in kern}
 
     conv = conv_leg(args, base, dfl) if args.conv_steps else None
+    viterbi = viterbi_leg(args, base, dfl, devs[0], d, ws) if args.viterbi_steps else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -328,6 +358,7 @@ def main():
         "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "mean_accept_len": round(mean_accept, 3),
         "conv2tap": conv,
+        "trace_viterbi": viterbi,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -22,7 +22,7 @@ K_MAX, L_MAX, R_MAX, V_MAX, CHUNK = 16, 16, 256, 2097152, 4096
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 KERNELS = ("topk", "gate", "scores", "trace", "stats", "finalize", "cycle_stream", "cycle_scores",
-           "cycle_finalize", "conv2tap")
+           "cycle_finalize", "conv2tap", "trace_viterbi")
 
 
 class dflash_dims(ctypes.Structure):
@@ -57,6 +57,7 @@ def _load():
         "dflash_verify": (I32, [D, P, P, P, P, P, P, U64, P, P, P, SZ, P]),
         "dflash_cycle": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dflash_conv2tap": (I32, [D, P, P, P, P, P]),
+        "dflash_trace_viterbi": (I32, [D, P, P, P, P, P, P]),
         "dflash_read_probe": (I32, [P, SZ, P, P]),
         "dflash_copy_probe": (I32, [P, P, SZ, P]),
         "dflash_kernel_name": (ctypes.c_char_p, [I32]),
@@ -189,6 +190,15 @@ def dflash_cycle(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws
         _ptr(draft_tok, "draft_tok", torch.int32, R, optional=True),
         _ptr(q, "q", torch.float32, R * d.K, optional=True),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
+
+
+def dflash_trace_viterbi(d, S, cand_idx, path_rank, draft_tok, q, stream=None):
+    R = d.B * d.L
+    _check(lib.dflash_trace_viterbi(ctypes.byref(d), _ptr(S, "S", torch.float32, R * d.K * d.K),
+                                    _ptr(cand_idx, "cand_idx", torch.int32, R * d.K),
+                                    _ptr(path_rank, "path_rank", torch.int32, R),
+                                    _ptr(draft_tok, "draft_tok", torch.int32, R),
+                                    _ptr(q, "q", torch.float32, R * d.K), _stream(stream)))
 
 
 def dflash_conv2tap(d, x, x0, Wt, y, stream=None):

@@ -285,6 +285,22 @@ dflash_status dflash_trace(const dflash_dims* d, const float* S, const int32_t* 
   }
 }
 
+dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
+                                   int32_t* draft_tok, float* q, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (dflash_status s = check_ptrs({{S, "S", false}, {cand_idx, "cand_idx", false}, {path_rank, "path_rank", false},
+                                      {draft_tok, "draft_tok", false}, {q, "q", false}})) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_TRACE_VITERBI, st, [&] {
+      return dfk::launch_trace_viterbi(*d, S, cand_idx, path_rank, draft_tok, q, st);
+    }), "viterbi trace launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
 dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* cand_idx, const int32_t* path_rank,
                             const float* q, const float* T, const uint64_t* seed, uint64_t cycle,
                             int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes, void* stream) {
@@ -383,7 +399,8 @@ dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* 
 
 const char* dflash_kernel_name(int32_t kernel) {
   static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize",
-                                                   "cycle_stream", "cycle_scores", "cycle_finalize", "conv2tap"};
+                                                   "cycle_stream", "cycle_scores", "cycle_finalize", "conv2tap",
+                                                   "trace_viterbi"};
   return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
 }
 

@@ -9,27 +9,38 @@
 //
 // bf16 operands: the taps are a GEMM [B*L, H] x [H, 2H] on the matrix cores
 // (v_mfma_f32_16x16x32_bf16) with the mixing fused into its epilogue, so
-// neither the taps nor a transposed copy ever reach HBM.  A block owns 64
-// rows (four 16-row MFMA tiles) and 16 channels of both taps (two 16-column
-// tiles, rows c and H + c of Wt); its four waves split the k range
-// (interleaved 32-wide steps) and their partial tiles are summed through
-// LDS in wave order.  Both operands are k-contiguous, so every fragment is
-// one 16-byte load per lane.  The row tiles of one channel tile are placed
-// on one XCD (block id mod 8), so that tile's Wt rows come from HBM once and
-// from that XCD's L2 after.
+// neither the taps nor a transposed copy ever reach HBM.  A block of four
+// waves (2 x 2) owns BM rows and BC channels of both taps; every 64-wide k
+// stage of its x rows and generator rows is loaded with whole 128-byte row
+// pieces (eight lanes per row) into LDS (16-byte chunks XOR-swizzled by row,
+// so that neither the row-piece stores nor the fragment reads conflict in
+// the banks), double-buffered, with P stages of loads in flight in
+// registers while the MFMAs read the current one.  A wave owns MT row tiles and CT channel tiles of both taps,
+// so the two taps of each output sit in the same lane and the epilogue
+// mixes them from registers.  The row tiles of one channel tile share an XCD (block id mod 8), so that
+// tile's generator rows come from HBM once and from that XCD's L2 after.
 // fp32 operands: one thread per output, two dot products on the VALU.
 #include "device_util.hpp"
 #include "internal.hpp"
 #include "select_blocks.hpp"
 
+
 namespace dfk {
 
 namespace {
 
-constexpr int kConvRowTiles = 4;              // 16-row MFMA tiles per block
-constexpr int kConvRows = 16 * kConvRowTiles;  // rows per block
-constexpr int kConvCh = 16;                    // channels per block (each tap)
-constexpr int kConvWaves = 4;
+constexpr int kConvBK = 64;                // k per LDS stage (two MFMA k-steps)
+
+// MT 16-row tiles and CT 16-channel tiles (each with both taps) per wave;
+// the block's 2 x 2 waves cover BM rows and BC channels
+template <int MT, int CT>
+struct ConvTile {
+  static constexpr int BM = 32 * MT;
+  static constexpr int BC = 32 * CT;
+  static constexpr int ROWS = BM + 2 * BC;  // staged rows: x rows, then tap-0 and tap-1 generator rows
+  static constexpr int LOADS = ROWS * (kConvBK / 8) / 256;  // 16-byte loads per thread per stage
+  static_assert(BM % 32 == 0 && (2 * BC) % 32 == 0, "a load instruction covers 32 rows of one operand");
+};
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -43,85 +54,164 @@ __device__ __forceinline__ bool conv_tile(int id, int n_rt, int n_ct, int& rt, i
   return ct < n_ct;
 }
 
+// Workgroup barrier for LDS hand-offs only: this wave's LDS reads and
+// writes complete (lgkmcnt 0), then s_barrier.  __syncthreads() would also
+// wait for every global load in flight (vmcnt 0), which drains the prefetch
+// ring at every stage.  The empty asm keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MT, int CT, int P>
 __global__ __launch_bounds__(256) void conv_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ x0,
                                                         const uint16_t* __restrict__ Wt, int R, int L, int H, int n_rt,
                                                         int n_ct, float* __restrict__ y) {
-  __shared__ float red[kConvWaves][kConvRowTiles * 2][4][kWave];  // 32 KB
+  using Tl = ConvTile<MT, CT>;
+  constexpr int PITCH = kConvBK * 2;  // 128-byte rows, 16-byte chunks XOR-swizzled by row % 8
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][Tl::ROWS * PITCH];
   int rt, ct;
   if (!conv_tile(blockIdx.x, n_rt, n_ct, rt, ct)) return;  // padding ids of the last channel group
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = rt * kConvRows, ch0 = ct * kConvCh;
-  const int kl = (lane >> 4) * 8;  // this lane's k offset inside a 32-wide step
-  // operand rows of this lane: four x rows (one per row tile) and the two
-  // generator rows of channel ch0 + lane % 16 (clamped in range; masked below)
-  const uint16_t* ap[kConvRowTiles];
-  bool aok[kConvRowTiles];
+  const int wm = wave & 1, wn = wave >> 1;
+  const int row0 = rt * Tl::BM, ch0 = ct * Tl::BC;
+  const int n_st = (H + kConvBK - 1) / kConvBK;
+
+  // this thread's share of a stage: LOADS row pieces of 16 bytes; staged row
+  // rho = p / 8 holds x row row0 + rho, then the tap-0 generator rows
+  // ch0 + j and the tap-1 rows H + ch0 + j
+  const uint16_t* src[Tl::LOADS];
+  unsigned rmask[Tl::LOADS];  // all ones for a row inside the operand, else zero
+  int dst[Tl::LOADS];
+  const int c8 = (tid & 7) * 8;
 #pragma unroll
-  for (int i = 0; i < kConvRowTiles; ++i) {
-    const int row = row0 + i * 16 + (lane & 15);
-    aok[i] = row < R;
-    ap[i] = x + (size_t)min(row, R - 1) * H + kl;
-  }
-  const int ch = ch0 + (lane & 15);
-  const bool bok = ch < H;
-  const uint16_t* bp0 = Wt + (size_t)min(ch, H - 1) * H + kl;
-  const uint16_t* bp1 = bp0 + (size_t)H * H;
-  const bf16x8 zero = {};
-  v4f32 acc[kConvRowTiles][2];
-#pragma unroll
-  for (int i = 0; i < kConvRowTiles; ++i) acc[i][0] = acc[i][1] = (v4f32){0.f, 0.f, 0.f, 0.f};
-  const int n_steps = (H + 31) / 32;
-  // two k-steps per iteration: every operand of both loaded before the
-  // first MFMA
-  for (int s0 = wave; s0 < n_steps; s0 += 2 * kConvWaves) {
-    bf16x8 a[2][kConvRowTiles], b[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int s = s0 + u * kConvWaves;
-      const int k = s * 32;
-      const bool kok = s < n_steps && k + kl < H;
-#pragma unroll
-      for (int i = 0; i < kConvRowTiles; ++i)
-        a[u][i] = kok && aok[i] ? *reinterpret_cast<const bf16x8*>(ap[i] + k) : zero;
-      b[u][0] = kok && bok ? *reinterpret_cast<const bf16x8*>(bp0 + k) : zero;
-      b[u][1] = kok && bok ? *reinterpret_cast<const bf16x8*>(bp1 + k) : zero;
+  for (int i = 0; i < Tl::LOADS; ++i) {
+    const int rho = (tid >> 3) + 32 * i;
+    dst[i] = rho * PITCH + ((tid & 7) ^ (rho & 7)) * 16;
+    if (rho < Tl::BM) {
+      const int row = row0 + rho;
+      rmask[i] = row < R ? 0xFFFFFFFFu : 0u;
+      src[i] = x + (size_t)min(row, R - 1) * H + c8;
+    } else {
+      const int j = rho - Tl::BM, tap = j / Tl::BC, c = ch0 + j - tap * Tl::BC;
+      rmask[i] = c < H ? 0xFFFFFFFFu : 0u;
+      src[i] = Wt + ((size_t)tap * H + min(c, H - 1)) * H + c8;
     }
+  }
+  // P stages of loads in flight: register slot u % P holds stage u until
+  // it is stored to LDS, then takes stage u + P
+  uint4 pre[P][Tl::LOADS];
+  // loads are unconditional (a masked load would become a branch, and the
+  // compiler would then wait for every load in flight before each store):
+  // a k run past the row end reads the row's last eight values instead,
+  // and the store writes zeros for it and for rows past the edge
+  auto stage_k = [&](int s) { return s * kConvBK; };
+  auto load_stage = [&](int s, uint4(&r)[Tl::LOADS]) {
+    const int k0 = stage_k(s);
+    const int ko = k0 + c8 < H ? k0 : H - 8 - c8;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < Tl::LOADS; ++i) r[i] = *reinterpret_cast<const uint4*>(src[i] + ko);
+  };
+  auto store_stage = [&](const uint4(&r)[Tl::LOADS], int s, int buf) {
+    const unsigned kok = stage_k(s) + c8 < H ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int i = 0; i < kConvRowTiles; ++i)
+    for (int i = 0; i < Tl::LOADS; ++i) {
+      const unsigned m = kok & rmask[i];
+      *reinterpret_cast<uint4*>(&lds[buf][dst[i]]) = make_uint4(r[i].x & m, r[i].y & m, r[i].z & m, r[i].w & m);
+    }
+  };
+
+  v4f32 acc[MT][CT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[m][c][0] = acc[m][c][1] = (v4f32){0.f, 0.f, 0.f, 0.f};
+  // fragment offsets: lane row lane % 16 (tile rows start at multiples of
+  // 16, so the row's swizzle key is lane % 8), 16-byte chunk
+  // 4 * ks + lane / 16 of the 64-wide stage
+  int fo[kConvBK / 32];
+#pragma unroll
+  for (int ks = 0; ks < kConvBK / 32; ++ks) {
+    const int c = 4 * ks + (lane >> 4);
+    fo[ks] = (lane & 15) * PITCH + (c ^ (lane & 7)) * 16;
+  }
+  const int a_row = wm * 16 * MT, b_row = Tl::BM + wn * 16 * CT;
+  auto compute = [&](const unsigned char* st) {
+    // every fragment of the stage first, then the MFMAs
+    bf16x8 a[kConvBK / 32][MT], b[kConvBK / 32][CT][2];
+#pragma unroll
+    for (int ks = 0; ks < kConvBK / 32; ++ks) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        a[ks][m] = *reinterpret_cast<const bf16x8*>(st + (a_row + m * 16) * PITCH + fo[ks]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int tap = 0; tap < 2; ++tap)
-          acc[i][tap] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][tap], acc[i][tap], 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kConvRowTiles; ++i)
-#pragma unroll
-    for (int tap = 0; tap < 2; ++tap)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][i * 2 + tap][e][lane] = acc[i][tap][e];
-  __syncthreads();
-  // epilogue: 64 rows x 16 channels, four outputs per thread; the MFMA
-  // tile holds (row 4 * (lane / 16) + e, column lane % 16) in element e
-#pragma unroll
-  for (int o = 0; o < kConvRows * kConvCh / 256; ++o) {
-    const int p = tid + o * 256;
-    const int rl = p / kConvCh, cl = p - (p / kConvCh) * kConvCh;
-    const int row = row0 + rl, c = ch0 + cl;
-    if (row >= R || c >= H) continue;
-    const int i = rl >> 4, rr = rl & 15;
-    const int ln = (rr >> 2) * 16 + cl, e = rr & 3;
-    float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < kConvWaves; ++w) {
-      w0 += red[w][i * 2][e][ln];
-      w1 += red[w][i * 2 + 1][e][ln];
+          b[ks][c][tap] = *reinterpret_cast<const bf16x8*>(st + (b_row + tap * Tl::BC + c * 16) * PITCH + fo[ks]);
     }
-    const int t = row % L;
-    const float xv = bf16_to_f32(x[(size_t)row * H + c]);
-    const float xp = bf16_to_f32(t > 0 ? x[(size_t)(row - 1) * H + c] : x0[(size_t)(row / L) * H + c]);
-    y[(size_t)row * H + c] = fmaf(w1, xp, w0 * xv);
+#pragma unroll
+    for (int ks = 0; ks < kConvBK / 32; ++ks)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int tap = 0; tap < 2; ++tap)
+            acc[m][c][tap] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][m], b[ks][c][tap], acc[m][c][tap], 0, 0, 0);
+  };
+
+  // straight-line ring (P divides the stage count, so no stage test inside
+  // the unrolled body): the last P stages reload the final stage into slots
+  // that are never stored, and the last store fills a buffer nobody reads
+#pragma unroll
+  for (int u = 0; u < P; ++u) load_stage(u, pre[u]);
+  store_stage(pre[0], 0, 0);
+  lds_barrier();
+  for (int s0 = 0; s0 < n_st; s0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int s = s0 + u;
+      load_stage(min(s + P, n_st - 1), pre[u]);  // stage s is in LDS already
+      compute(lds[s & 1]);
+      store_stage(pre[(u + 1) % P], min(s + 1, n_st - 1), (s + 1) & 1);
+      lds_barrier();
+    }
   }
+
+  // epilogue: element e of the lane holds (row 4 * (lane / 16) + e, channel
+  // lane % 16) of each tile; both taps of that output are in this lane
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int ch = ch0 + wn * 16 * CT + c * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + wm * 16 * MT + m * 16 + 4 * (lane >> 4) + e;
+        if (row >= R || ch >= H) continue;
+        const int t = row % L;
+        const float xv = bf16_to_f32(x[(size_t)row * H + ch]);
+        const float xp = bf16_to_f32(t > 0 ? x[(size_t)(row - 1) * H + ch] : x0[(size_t)(row / L) * H + ch]);
+        y[(size_t)row * H + ch] = fmaf(acc[m][c][1][e], xp, acc[m][c][0][e] * xv);
+      }
+    }
+}
+
+template <int MT, int CT, int P>
+hipError_t launch_conv_mfma(const void* x, const void* x0, const void* Wt, int R, int L, int H, float* y,
+                            hipStream_t st) {
+  using Tl = ConvTile<MT, CT>;
+  const int n_rt = (R + Tl::BM - 1) / Tl::BM;
+  const int n_ct = (H + Tl::BC - 1) / Tl::BC;
+  const long long blocks = (long long)((n_ct + 7) / 8) * 8 * n_rt;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  launch(conv_mfma_kernel<MT, CT, P>, dim3((unsigned)blocks), dim3(256), st, reinterpret_cast<const uint16_t*>(x),
+         reinterpret_cast<const uint16_t*>(x0), reinterpret_cast<const uint16_t*>(Wt), R, L, H, n_rt, n_ct, y);
+  return hipSuccess;
 }
 
 __global__ __launch_bounds__(256) void conv_f32_kernel(const float* __restrict__ x, const float* __restrict__ x0,
@@ -148,12 +238,22 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
                            hipStream_t st) {
   const int R = d.B * d.L, H = d.hidden;
   if (d.param_dtype == DFLASH_BF16) {
-    const int n_rt = (R + kConvRows - 1) / kConvRows;
-    const int n_ct = (H + kConvCh - 1) / kConvCh;
-    const long long blocks = (long long)((n_ct + 7) / 8) * 8 * n_rt;
-    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    launch(conv_mfma_kernel, dim3((unsigned)blocks), dim3(256), st, reinterpret_cast<const uint16_t*>(x),
-           reinterpret_cast<const uint16_t*>(x0), reinterpret_cast<const uint16_t*>(Wt), R, d.L, H, n_rt, n_ct, y);
+    // 128 x 64 blocks when they alone give every CU a block, else 64 x 32
+    const long long big = (long long)((R + 127) / 128) * ((H + 63) / 64);
+    // P stages of loads in flight, P dividing the stage count (measured
+    // best: 4 for the 64 x 32 blocks, 2 for the 128 x 64 blocks, whose
+    // registers allow two waves per SIMD only up to that depth)
+    const int n_st = (H + kConvBK - 1) / kConvBK;
+    hipError_t e;
+    if (big >= 256) {
+      e = n_st % 2 == 0 ? launch_conv_mfma<4, 2, 2>(x, x0, Wt, R, d.L, H, y, st)
+                        : launch_conv_mfma<4, 2, 1>(x, x0, Wt, R, d.L, H, y, st);
+    } else {
+      e = n_st % 4 == 0   ? launch_conv_mfma<2, 1, 4>(x, x0, Wt, R, d.L, H, y, st)
+          : n_st % 2 == 0 ? launch_conv_mfma<2, 1, 2>(x, x0, Wt, R, d.L, H, y, st)
+                          : launch_conv_mfma<2, 1, 1>(x, x0, Wt, R, d.L, H, y, st);
+    }
+    if (e != hipSuccess) return e;
   } else {
     launch(conv_f32_kernel, dim3((unsigned)((H + 255) / 256), (unsigned)R), dim3(256), st,
            reinterpret_cast<const float*>(x), reinterpret_cast<const float*>(x0), reinterpret_cast<const float*>(Wt),

@@ -77,6 +77,8 @@ hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, flo
 hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t* cand_idx,
                          const float* cand_logit, const void* E, const float* gpart, float* S,
                          hipStream_t st);
+hipError_t launch_trace_viterbi(const dflash_dims& d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
+                                int32_t* draft_tok, float* q, hipStream_t st);
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
                         const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
                         float* q, hipStream_t st);

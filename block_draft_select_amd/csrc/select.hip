@@ -66,13 +66,16 @@ __global__ __launch_bounds__(64) void trace_kernel(const float* __restrict__ S, 
   const float Tb = T[b];
   const size_t s0 = (size_t)b * L * K * K;
   const int n = L * K * K;
-  float sv[NMAX / 64];  // every load issued before the first store
+  // every load issued before the first store; indices past the stream's
+  // arrays are clamped (a masked load would become a branch, and each
+  // branch would wait for the loads before it)
+  float sv[NMAX / 64];
 #pragma unroll
-  for (int s = 0; s < NMAX / 64; ++s) sv[s] = lane + s * 64 < n ? S[s0 + lane + s * 64] : 0.f;
+  for (int s = 0; s < NMAX / 64; ++s) sv[s] = S[s0 + min(lane + s * 64, n - 1)];
   int cv[DFLASH_L_MAX * DFLASH_K_MAX / 64];
 #pragma unroll
   for (int s = 0; s < DFLASH_L_MAX * DFLASH_K_MAX / 64; ++s)
-    cv[s] = lane + s * 64 < L * K ? clamp_idx(cand_idx[(size_t)b * L * K + lane + s * 64], V) : 0;
+    cv[s] = clamp_idx(cand_idx[(size_t)b * L * K + min(lane + s * 64, L * K - 1)], V);
 #pragma unroll
   for (int s = 0; s < NMAX / 64; ++s)
     if (lane + s * 64 < n) Ss[lane + s * 64] = sv[s];

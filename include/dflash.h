@@ -183,6 +183,27 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
 
 /* ---- measurement helpers (not part of the method) ---------------------- */
 
+/* Max-sum (Viterbi) variant of the trace (P3 "DFlash 2: Keep Drafting
+ * Parallel", "What Comes Next", paragraph "A Lightweight Path Selector": the
+ * pair scores and a walk from the verified token; better searches are left
+ * open there).  Instead of the greedy walk, the path of largest summed edge
+ * score S[0, 0, j_1] + S[1, j_1, j_2] + ... + S[L-1, j_{L-1}, j_L] over all
+ * K^L paths; among equal values the smallest in reverse lexicographic order
+ * (j_L first).  Sums are formed in fp64 from the fp32 scores.  The path is
+ * deterministic, so q is one-hot at each chosen rank and dflash_verify keeps
+ * the target distribution exact at any temperature.
+ *   d          uses B, L, V, K (the whole struct is validated)
+ *   S          [B, L, K, K] fp32, as written by dflash_pair_scores
+ *   cand_idx   [B, L, K] i32 (indices outside [0, V) are clamped for draft_tok)
+ *   path_rank  [B, L] i32, written: the chosen rank per position
+ *   draft_tok  [B, L] i32, written: cand_idx at that rank
+ *   q          [B, L, K] fp32, written: one-hot at path_rank
+ * Caller-owned device buffers; one launch on `stream` (one wave per stream);
+ * no workspace; no random numbers.  Scores must be finite.  Invalid
+ * arguments launch nothing and leave the outputs untouched. */
+dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
+                                   int32_t* draft_tok, float* q, void* stream);
+
 /* The two-tap dynamic depthwise convolution of the drafter's block
  * representations (P1 "DFlash 2: Block diffusion, wearing a drafter's coat",
  * "The architecture", "Suffix-decay convolution"; P2 "A 2B Drafter Made a
@@ -226,7 +247,8 @@ enum {
   DFLASH_KERNEL_CYCLE_SCORES = 7,   /* dflash_cycle: candidates + pair scores */
   DFLASH_KERNEL_CYCLE_FINALIZE = 8, /* dflash_cycle: trace + verify */
   DFLASH_KERNEL_CONV2TAP = 9,       /* dflash_conv2tap */
-  DFLASH_KERNEL_COUNT = 10
+  DFLASH_KERNEL_TRACE_VITERBI = 10, /* dflash_trace_viterbi */
+  DFLASH_KERNEL_COUNT = 11
 };
 
 /* Name of a kernel identifier ("" if out of range). */
