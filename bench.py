@@ -205,6 +205,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="input configuration id (1..5)")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for 2x LLC)")
+    ap.add_argument("--L", type=int, default=0, help="drafted positions per block (0: the configuration's)")
     ap.add_argument("--profile-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -231,10 +232,11 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    base = synth.make(args.config, set_id=0)
+    kw = {"L": args.L} if args.L else {}
+    base = synth.make(args.config, set_id=0, **kw)
     ub, zb = logit_bytes(base)
     n_sets = args.sets or max(1, min(64, -(-2 * LLC_BYTES // (ub + zb))))
-    sets = [base] + [synth.make(args.config, set_id=s, plant=None) for s in range(1, n_sets)]
+    sets = [base] + [synth.make(args.config, set_id=s, plant=None, **kw) for s in range(1, n_sets)]
     devs = [device_inputs(s) for s in sets]
     _log(f"[bench] {workload_name(base)}; {n_sets} input sets generated in {time.perf_counter() - t_gen:.1f} s")
 

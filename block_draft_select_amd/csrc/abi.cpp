@@ -144,9 +144,14 @@ namespace dfk {
 thread_local hipEvent_t g_launch_start = nullptr, g_launch_stop = nullptr;
 
 // Sub-segments per top-K block: by default the smallest multiple of 4 that
-// keeps the top-K part of the grid at or below 2048 blocks; at least enough
-// that a row has at most kTopkMaxSeg blocks.  DFLASH_TOPK_SPB overrides the
-// default for tuning sweeps.
+// keeps the top-K part of the grid at or below 2048 blocks; raised so that
+// a row has at most 8 partial lists when the top-K part still has 512 or
+// more blocks (the scores launch searches more than 8 lists 16 at a time,
+// about 2.5 us more at 151936 tokens, which outweighs the longer top-K
+// blocks once the grid is that large: +5% cycles/s at 4 and 5 drafted
+// positions of 32 streams, -6% at one stream); at least enough that a row
+// has at most kTopkMaxSeg blocks.  DFLASH_TOPK_SPB overrides the default
+// for tuning sweeps.
 static int topk_spb(size_t rows, int n_sub) {
   static const int env = [] {
     const char* s = std::getenv("DFLASH_TOPK_SPB");
@@ -157,6 +162,8 @@ static int topk_spb(size_t rows, int n_sub) {
     spb = env;
   } else {
     while (spb < n_sub && rows * (size_t)((n_sub + spb - 1) / spb) > 2048) spb += 4;
+    const int spb8 = ((n_sub + 7) / 8 + 3) / 4 * 4;
+    if (spb < spb8 && rows * (size_t)((n_sub + spb8 - 1) / spb8) >= 512) spb = spb8;
   }
   const int min_spb = (n_sub + kTopkMaxSeg - 1) / kTopkMaxSeg;
   return spb < min_spb ? min_spb : spb;

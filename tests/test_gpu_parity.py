@@ -91,6 +91,22 @@ def test_full_size_configs_sampled(name, cid, streams):
         compare_stream(gpu, ref[b], b)
 
 
+# block sizes the serving runtimes use (blocks of 4 to 16 drafted
+# positions) at the concurrent-32 shapes, on sampled streams
+BLOCKS = [4, 5, 7]
+
+
+@pytest.mark.parametrize("L", BLOCKS, ids=[f"L{L}" for L in BLOCKS])
+def test_block_size_sweep_sampled(L):
+    inp = synth.make(3, set_id=0, L=L)
+    streams = [0, 17, 31]
+    _say(f"[parity] block sweep: B={inp['B']} L={inp['L']} V={inp['V']} streams={streams}")
+    ref, _ = guarded(inp, streams=streams)
+    gpu = run_cycle(inp)
+    for b in ref:
+        compare_stream(gpu, ref[b], b)
+
+
 # limits of the boundary: every token a candidate (the residual has no
 # chunk mass), the largest vocabulary (more chunk terms than the finalize
 # keeps in LDS), and the largest row count B (L + 1) = 65535
