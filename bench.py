@@ -206,6 +206,11 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="input configuration id (1..5)")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for 2x LLC)")
     ap.add_argument("--L", type=int, default=0, help="drafted positions per block (0: the configuration's)")
+    ap.add_argument("--B", type=int, default=0,
+                    help="streams (0: the configuration's); B/N is one GPU's share when streams shard over N GPUs")
+    ap.add_argument("--V", type=int, default=0,
+                    help="vocabulary (0: the configuration's); V/N is one GPU's share when the vocabulary shards "
+                         "over N GPUs")
     ap.add_argument("--profile-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -232,7 +237,7 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    kw = {"L": args.L} if args.L else {}
+    kw = {k: v for k, v in (("L", args.L), ("B", args.B), ("V", args.V)) if v}
     base = synth.make(args.config, set_id=0, **kw)
     ub, zb = logit_bytes(base)
     n_sets = args.sets or max(1, min(64, -(-2 * LLC_BYTES // (ub + zb))))

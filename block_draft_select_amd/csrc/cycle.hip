@@ -119,19 +119,25 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
   const int nk = n_seg * 16;
   const uint64_t* l0 = partial + (size_t)(t > 0 ? bt - 1 : bt) * nk;
   const uint64_t* l1 = partial + (size_t)bt * nk;
+  // unconditional loads from clamped slots, masked afterwards (a masked
+  // load would be a branch that waits for the loads issued before it)
   uint64_t kv[KPT];
 #pragma unroll
   for (int q = 0; q < KPT; ++q) {
     const int i = tid + q * 256;
-    kv[q] = i < nk ? (t > 0 ? l0[i] : 0ull) : (i < 2 * nk ? l1[i - nk] : 0ull);
+    kv[q] = i < nk ? l0[i] : l1[min(i - nk, nk - 1)];
   }
   const float Tb = T[b];
   const uint64_t sd = seed[b];
   const uint32_t u = stream_block(sd, cycle, (uint32_t)(t + 1), 0u).x;  // the trace uniform of position t
   edge_gate(cl.e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
+  // masked only here, after the gate's loads are in flight too: edge 0 has
+  // no predecessor row (its keys read as empty)
 #pragma unroll
-  for (int q = 0; q < KPT; ++q)
-    if (tid + q * 256 < 2 * nk) cl.keys[tid + q * 256] = kv[q];
+  for (int q = 0; q < KPT; ++q) {
+    const int i = tid + q * 256;
+    if (i < 2 * nk) cl.keys[i] = i < nk && t == 0 ? 0ull : kv[q];
+  }
   __syncthreads();
   merge_two_staged<WIDE>(cl.keys, n_seg, K, cl.prev, cl.cur);
   // every thread reads the merged lists itself (no second hand-off):

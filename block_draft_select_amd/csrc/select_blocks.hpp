@@ -110,10 +110,12 @@ __device__ __forceinline__ float gate_value(const float* __restrict__ part, int 
   const float* p = part + (size_t)row * r + col;
   float z = 0.f;
   for (int k0 = 0; k0 < n_ks; k0 += 8) {  // eight slices' loads in flight at once
+    // unconditional loads (slices past the last re-read it and are not
+    // added): a masked load would be a branch that waits for the loads
+    // issued before it
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = k0 + i < n_ks ? p[(k0 + i) * stride] : 0.f;
+    for (int i = 0; i < 8; ++i) v[i] = p[(size_t)min(k0 + i, n_ks - 1) * stride];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (k0 + i < n_ks) z += v[i];

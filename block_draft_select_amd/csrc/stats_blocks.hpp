@@ -327,9 +327,9 @@ __device__ __forceinline__ const float* q_row_of(const FinLds& f, int t, int K) 
 // One block per stream.  WITH_TRACE: the block also walks the trace over
 // the decided trace table (jstar: decision of every row (t, i); qtab: the
 // q of every row, [B, L, K, K]) and writes path_rank / draft_tok / q;
-// otherwise path_rank and q are inputs.  zc_pre, if given, holds the
-// candidates' target logits [B, L, K] (fp32-exact values), else they are
-// gathered here.
+// otherwise path_rank and q are inputs.  With WITH_TRACE, zc_pre holds the
+// candidates' target logits [B, L, K] (fp32-exact values); otherwise it is
+// not read and they are gathered here.
 template <int DT, bool WITH_TRACE>
 __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, int L, int V, int K, int n_chunk,
                                 const float* __restrict__ T, const uint64_t* __restrict__ seed, uint64_t cycle,
@@ -350,42 +350,56 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   const int n_terms = (L + 1) * n_chunk;
   const bool cached = n_terms <= kTermCache;
 
-  // (0) every independent load at once, and all random blocks
-  if (tid < L * K) {
-    const int t = tid / K, k = tid - (tid / K) * K;
-    const size_t e = (size_t)b * L * K + tid;
-    const int ci = clamp_idx(cand_idx[e], V);
-    f.cand[t][k] = ci;
-    if (!WITH_TRACE) f.qs[t][k] = q[e];
-    if (!greedy) f.zc[t][k] = zc_pre ? (double)zc_pre[e] : logit_at<DT>(Z, (zrow0 + t) * Vs + ci);
-  }
-  if (!WITH_TRACE && tid < L) f.rank[tid] = clamp_idx(path_rank[(size_t)b * L + tid], K);
+  // (0) every independent load at once, and all random blocks.  Loads are
+  // unconditional, from clamped (in-range) indices, and land in registers
+  // before any store: a masked load, or a store that needs a load's value
+  // inside a branch, would be a branch that waits for the loads issued
+  // before it
+  const int lk = L * K;
+  const size_t e0 = (size_t)b * lk;
+  const int ei = min(tid, lk - 1);
+  const int ci_raw = cand_idx[e0 + ei];
+  // with the trace (the fused cycle) the scores launch has gathered the
+  // candidates' target logits into zc_pre; the split verify reads them from Z
+  const float zc_raw = WITH_TRACE ? zc_pre[e0 + ei] : 0.f;
+  const float q_raw = WITH_TRACE ? 0.f : q[e0 + ei];
+  const int pr_raw = WITH_TRACE ? 0 : path_rank[(size_t)b * L + min(tid, L - 1)];
+  constexpr int NS = DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX / kFinThreads;
+  const size_t s0 = (size_t)b * lk * K;
+  const int n = lk * K;
+  float sv[NS];
+  int js = 0;
   if (WITH_TRACE) {
-    // fixed trip counts so that every load is issued before the first store
-    constexpr int NS = DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX / kFinThreads;
-    const size_t s0 = (size_t)b * L * K * K;
-    const int n = L * K * K;
-    float sv[NS];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) sv[k] = tid + k * kFinThreads < n ? qtab[s0 + tid + k * kFinThreads] : 0.f;
-    const int js = tid < L * K ? jstar[(size_t)b * L * K + tid] : 0;
+    for (int k = 0; k < NS; ++k) sv[k] = qtab[s0 + min(tid + k * kFinThreads, n - 1)];
+    js = jstar[e0 + ei];
+  }
+  constexpr int NC = kTermCache / kFinThreads;
+  float2 mv[NC];
+  if (cached) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k)
-      if (tid + k * kFinThreads < n) f.S[tid + k * kFinThreads] = sv[k];
-    if (tid < L * K) f.jstar[tid] = min(max(js, 0), K - 1);
+    for (int k = 0; k < NC; ++k)
+      mv[k] = *reinterpret_cast<const float2*>(&st_all[min(tid + k * kFinThreads, n_terms - 1)]);
   }
   if (!greedy) {
     if (tid >= 64 && tid < 64 + L) f.rnd0[tid - 64] = stream_block(sd, cycle, (uint32_t)(tid - 63), 0u);
     if (tid >= 128 && tid <= 128 + L) f.rnd1[tid - 128] = stream_block(sd, cycle, (uint32_t)(tid - 127), 1u);
   }
-  if (cached) {
-    constexpr int NC = kTermCache / kFinThreads;
-    float2 mv[NC];
+  if (tid < lk) {
+    const int t = tid / K, k = tid - (tid / K) * K;
+    const int ci = clamp_idx(ci_raw, V);
+    f.cand[t][k] = ci;
+    if (!WITH_TRACE) f.qs[t][k] = q_raw;
+    if (!greedy) f.zc[t][k] = WITH_TRACE ? (double)zc_raw : logit_at<DT>(Z, (zrow0 + t) * Vs + ci);
+  }
+  if (!WITH_TRACE && tid < L) f.rank[tid] = clamp_idx(pr_raw, K);
+  if (WITH_TRACE) {
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int i = tid + k * kFinThreads;
-      mv[k] = i < n_terms ? *reinterpret_cast<const float2*>(&st_all[i]) : make_float2(0.f, 0.f);
-    }
+    for (int k = 0; k < NS; ++k)
+      if (tid + k * kFinThreads < n) f.S[tid + k * kFinThreads] = sv[k];
+    if (tid < lk) f.jstar[tid] = min(max(js, 0), K - 1);
+  }
+  if (cached) {
 #pragma unroll
     for (int k = 0; k < NC; ++k)
       if (tid + k * kFinThreads < n_terms) f.ms[tid + k * kFinThreads] = mv[k];
