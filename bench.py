@@ -334,6 +334,24 @@ def main():
 
     conv = conv_leg(args, base, dfl) if args.conv_steps else None
     viterbi = viterbi_leg(args, base, dfl, devs[0], d, ws) if args.viterbi_steps else None
+    maxsum = None
+    if args.viterbi_steps:
+        # the whole cycle with the max-sum trace, same rotating inputs
+        def step_maxsum(i):
+            dv = devs[i % n_sets]
+            dfl.dflash_cycle_maxsum(d, dv["U"], dv["Z"], dv["x0"], dv["E"], dv["W"], dv["h"], dv["T"], dv["seed"],
+                                    i, out["accept_len"], out["out_tok"], ws)
+        for i in range(args.warmup):
+            step_maxsum(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step_maxsum(args.warmup + i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        maxsum = {"value": round(args.steps / el, 2), "unit": "cycles/s",
+                  "us_per_cycle": round(el * 1e6 / args.steps, 2)}
+        _log(f"[bench] max-sum cycle {maxsum['us_per_cycle']:.1f} us/cycle")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,6 +384,7 @@ def main():
         "mean_accept_len": round(mean_accept, 3),
         "conv2tap": conv,
         "trace_viterbi": viterbi,
+        "cycle_maxsum": maxsum,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_sha(),
     }

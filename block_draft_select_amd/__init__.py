@@ -56,6 +56,7 @@ def _load():
         "dflash_trace": (I32, [D, P, P, P, P, U64, P, P, P, P]),
         "dflash_verify": (I32, [D, P, P, P, P, P, P, U64, P, P, P, SZ, P]),
         "dflash_cycle": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dflash_cycle_maxsum": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dflash_conv2tap": (I32, [D, P, P, P, P, P]),
         "dflash_trace_viterbi": (I32, [D, P, P, P, P, P, P]),
         "dflash_read_probe": (I32, [P, SZ, P, P]),
@@ -171,11 +172,10 @@ def dflash_verify(d, Z, cand_idx, path_rank, q, T, seed, cycle, accept_len, out_
                              _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
 
 
-def dflash_cycle(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
-                 cand_idx=None, cand_logit=None, S=None, path_rank=None, draft_tok=None, q=None,
-                 stream=None):
+def _cycle_call(fn, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
+                cand_idx, cand_logit, S, path_rank, draft_tok, q, stream):
     R, lt, pt = d.B * d.L, _TORCH_LOGIT[d.logit_dtype], _TORCH_LOGIT[d.param_dtype]
-    _check(lib.dflash_cycle(
+    _check(fn(
         ctypes.byref(d), _ptr(U, "U", lt, R * d.V), _ptr(Z, "Z", lt, d.B * (d.L + 1) * d.V),
         _ptr(x0, "x0", torch.int32, d.B), _ptr(E, "E", pt, d.V * d.r),
         _ptr(W_g, "W_g", pt, d.hidden * d.r), _ptr(h, "h", pt, R * d.hidden),
@@ -190,6 +190,20 @@ def dflash_cycle(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws
         _ptr(draft_tok, "draft_tok", torch.int32, R, optional=True),
         _ptr(q, "q", torch.float32, R * d.K, optional=True),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
+
+
+def dflash_cycle(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
+                 cand_idx=None, cand_logit=None, S=None, path_rank=None, draft_tok=None, q=None,
+                 stream=None):
+    _cycle_call(lib.dflash_cycle, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
+                cand_idx, cand_logit, S, path_rank, draft_tok, q, stream)
+
+
+def dflash_cycle_maxsum(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
+                        cand_idx=None, cand_logit=None, S=None, path_rank=None, draft_tok=None, q=None,
+                        stream=None):
+    _cycle_call(lib.dflash_cycle_maxsum, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
+                cand_idx, cand_logit, S, path_rank, draft_tok, q, stream)
 
 
 def dflash_trace_viterbi(d, S, cand_idx, path_rank, draft_tok, q, stream=None):

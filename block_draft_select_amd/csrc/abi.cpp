@@ -332,11 +332,14 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
   }
 }
 
-dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0, const void* E,
-                           const void* W_g, const void* h, const float* T, const uint64_t* seed, uint64_t cycle,
-                           int32_t* accept_len, int32_t* out_tok, int32_t* cand_idx_opt, float* cand_logit_opt,
-                           float* S_opt, int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt, void* ws,
-                           size_t ws_bytes, void* stream) {
+// dflash_cycle and dflash_cycle_maxsum: the streaming launch and the
+// candidate/score launch, then either the fused trace + verify launch or the
+// max-sum trace followed by the split verify's finalize
+static dflash_status cycle_impl(bool maxsum, const dflash_dims* d, const void* U, const void* Z, const int32_t* x0,
+                                const void* E, const void* W_g, const void* h, const float* T, const uint64_t* seed,
+                                uint64_t cycle, int32_t* accept_len, int32_t* out_tok, int32_t* cand_idx_opt,
+                                float* cand_logit_opt, float* S_opt, int32_t* path_rank_opt, int32_t* draft_tok_opt,
+                                float* q_opt, void* ws, size_t ws_bytes, void* stream) {
   try {
     g_err.clear();
     if (dflash_status s = check_dims(d)) return s;
@@ -359,13 +362,40 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, c
     if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
           return dfk::launch_cycle_scores(*d, w, x0, E, Z, T, seed, cycle, base, cand_idx, cand_logit, S, st);
         }), "scores launch")) return s;
-    return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
-      return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, path_rank, draft_tok, q,
-                                        accept_len, out_tok, st);
+    if (!maxsum)
+      return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
+        return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, path_rank, draft_tok, q,
+                                          accept_len, out_tok, st);
+      }), "finalize launch");
+    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TRACE_VITERBI, st, [&] {
+          return dfk::launch_trace_viterbi(*d, S, cand_idx, path_rank, draft_tok, q, st);
+        }), "viterbi trace launch")) return s;
+    const dfk::ChunkStat* stats = reinterpret_cast<const dfk::ChunkStat*>(base + w.stats);
+    return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
+      return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
     }), "finalize launch");
   } catch (...) {
     return fail(DFLASH_ERR_HIP, "internal error");
   }
+}
+
+dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0, const void* E,
+                           const void* W_g, const void* h, const float* T, const uint64_t* seed, uint64_t cycle,
+                           int32_t* accept_len, int32_t* out_tok, int32_t* cand_idx_opt, float* cand_logit_opt,
+                           float* S_opt, int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return cycle_impl(false, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, cand_idx_opt,
+                    cand_logit_opt, S_opt, path_rank_opt, draft_tok_opt, q_opt, ws, ws_bytes, stream);
+}
+
+dflash_status dflash_cycle_maxsum(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0,
+                                  const void* E, const void* W_g, const void* h, const float* T,
+                                  const uint64_t* seed, uint64_t cycle, int32_t* accept_len, int32_t* out_tok,
+                                  int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
+                                  int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return cycle_impl(true, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, cand_idx_opt,
+                    cand_logit_opt, S_opt, path_rank_opt, draft_tok_opt, q_opt, ws, ws_bytes, stream);
 }
 
 dflash_status dflash_conv2tap(const dflash_dims* d, const void* x, const void* x0, const void* Wt, float* y,

@@ -181,7 +181,20 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
                            int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* ---- measurement helpers (not part of the method) ---------------------- */
+/* The whole cycle with the max-sum trace (dflash_trace_viterbi) in place of
+ * the greedy/sampled walk: the streaming launch and the candidate/score
+ * launch of dflash_cycle, then the max-sum trace, then the verify of
+ * dflash_verify's finalize on the chunk statistics the streaming launch
+ * wrote.  Same arguments, layouts and workspace as dflash_cycle; q is
+ * one-hot.  Outputs equal those of dflash_topk, dflash_pair_scores,
+ * dflash_trace_viterbi and dflash_verify called in turn. */
+dflash_status dflash_cycle_maxsum(const dflash_dims* d, const void* U, const void* Z,
+                                  const int32_t* x0, const void* E, const void* W_g, const void* h,
+                                  const float* T, const uint64_t* seed, uint64_t cycle,
+                                  int32_t* accept_len, int32_t* out_tok,
+                                  int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
+                                  int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Max-sum (Viterbi) variant of the trace (P3 "DFlash 2: Keep Drafting
  * Parallel", "What Comes Next", paragraph "A Lightweight Path Selector": the
@@ -222,6 +235,8 @@ dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const i
  * nothing and leave y untouched. */
 dflash_status dflash_conv2tap(const dflash_dims* d, const void* x, const void* x0, const void* Wt, float* y,
                               void* stream);
+
+/* ---- measurement helpers (not part of the method) ---------------------- */
 
 /* Stream-read `bytes` (multiple of 16, 16-byte aligned) of `buf` once: the
  * achievable HBM read ceiling for the streaming launch's access shape (each

@@ -101,6 +101,9 @@ def test_null_and_misaligned_pointers_rejected(dfl):
     assert b"Wt is NULL" in dfl.lib.dflash_last_error()
     assert dfl.lib.dflash_conv2tap(ctypes.byref(d), odd, fake, fake, fake, None) == 1
     assert b"aligned" in dfl.lib.dflash_last_error()
+    assert dfl.lib.dflash_cycle_maxsum(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake, 0, fake,
+                                       fake, None, None, None, None, None, None, fake, 1 << 30, None) == 1
+    assert b"h is NULL" in dfl.lib.dflash_last_error()
     assert dfl.lib.dflash_trace_viterbi(ctypes.byref(d), fake, fake, fake, None, fake, None) == 1
     assert b"draft_tok is NULL" in dfl.lib.dflash_last_error()
     bad = dfl.dims(1, 17, 4096, 4, 16, 16, "bf16", "bf16")

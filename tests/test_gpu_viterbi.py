@@ -1,6 +1,7 @@
 """GPU parity of the max-sum (Viterbi) trace: ``dflash_trace_viterbi`` through
 the C ABI against the float64 oracle (``oracle.viterbi``), and the verify that
-follows it against ``oracle.dflash.verify_stream`` with the one-hot q.
+follows it against ``oracle.dflash.verify_stream`` with the one-hot q; the
+fused ``dflash_cycle_maxsum`` must equal that split path bit for bit.
 
 Bar: bit-exact path ranks, draft tokens, q (exactly one-hot), accept counts
 and emitted tokens.  The GPU sums fp32 scores in fp64 and the oracle sums
@@ -84,6 +85,21 @@ def _run_split(inp):
     return {k: v.cpu().numpy() for k, v in o.items()}
 
 
+def _run_fused(inp):
+    import torch
+    import block_draft_select_amd as dfl
+    d = dims_of(inp)
+    dev = device_inputs(inp)
+    o = alloc_outputs(inp)
+    ws = dfl.workspace(d)
+    dfl.dflash_cycle_maxsum(d, dev["U"], dev["Z"], dev["x0"], dev["E"], dev["W"], dev["h"], dev["T"], dev["seed"],
+                            inp["cycle"], o["accept_len"], o["out_tok"], ws, cand_idx=o["cand_idx"],
+                            cand_logit=o["cand_logit"], S=o["S"], path_rank=o["path_rank"],
+                            draft_tok=o["draft_tok"], q=o["q"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in o.items()}
+
+
 CASES = [
     # (name, config id, overrides, streams compared (None: all))
     ("tiny-f32", 1, dict(B=3), None),
@@ -104,6 +120,9 @@ def test_viterbi_then_verify_match_oracle(name, cid, kw, streams):
     _say(f"[viterbi] {name}: B={inp['B']} L={inp['L']} V={inp['V']} K={inp['K']}")
     ref = _guarded(inp, streams)
     gpu = _run_split(inp)
+    fused = _run_fused(inp)
+    for k, v in gpu.items():  # the fused max-sum cycle equals the split path bit for bit
+        np.testing.assert_array_equal(fused[k], v, err_msg=f"fused vs split: {k}")
     L = int(inp["L"])
     for b in streams:
         np.testing.assert_array_equal(gpu["cand_idx"][b], ref[b]["cand_idx"], err_msg=f"cand_idx {b}")
