@@ -332,9 +332,9 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
   }
 }
 
-// dflash_cycle and dflash_cycle_maxsum: the streaming launch and the
-// candidate/score launch, then either the fused trace + verify launch or the
-// max-sum trace followed by the split verify's finalize
+// dflash_cycle and dflash_cycle_maxsum: the streaming launch, the
+// candidate/score launch, then the trace + verify launch (walking the greedy
+// or sampled table, or finding the max-sum path over the scores)
 static dflash_status cycle_impl(bool maxsum, const dflash_dims* d, const void* U, const void* Z, const int32_t* x0,
                                 const void* E, const void* W_g, const void* h, const float* T, const uint64_t* seed,
                                 uint64_t cycle, int32_t* accept_len, int32_t* out_tok, int32_t* cand_idx_opt,
@@ -362,17 +362,9 @@ static dflash_status cycle_impl(bool maxsum, const dflash_dims* d, const void* U
     if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
           return dfk::launch_cycle_scores(*d, w, x0, E, Z, T, seed, cycle, base, cand_idx, cand_logit, S, st);
         }), "scores launch")) return s;
-    if (!maxsum)
-      return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
-        return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, path_rank, draft_tok, q,
-                                          accept_len, out_tok, st);
-      }), "finalize launch");
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_TRACE_VITERBI, st, [&] {
-          return dfk::launch_trace_viterbi(*d, S, cand_idx, path_rank, draft_tok, q, st);
-        }), "viterbi trace launch")) return s;
-    const dfk::ChunkStat* stats = reinterpret_cast<const dfk::ChunkStat*>(base + w.stats);
-    return hip_status(timed(DFLASH_KERNEL_FINALIZE, st, [&] {
-      return dfk::launch_finalize(*d, w, Z, cand_idx, path_rank, q, T, seed, cycle, stats, accept_len, out_tok, st);
+    return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
+      return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, maxsum ? S : nullptr, path_rank,
+                                        draft_tok, q, accept_len, out_tok, st);
     }), "finalize launch");
   } catch (...) {
     return fail(DFLASH_ERR_HIP, "internal error");

@@ -12,7 +12,8 @@
 //      next rank and q (S4).
 //   3. trace_finalize_kernel: one block per stream combines the chunk
 //      statistics (one wave per target row), walks the decided table (L
-//      look-ups), then runs the accept tests and the residual/bonus draw
+//      look-ups) or, for the max-sum cycle, finds the max-sum path over the
+//      pair scores, then runs the accept tests and the residual/bonus draw
 //      (S6).
 #include "stats_blocks.hpp"
 #include "topk_blocks.hpp"
@@ -173,7 +174,9 @@ __global__ __launch_bounds__(256) void cand_scores_kernel(const uint64_t* __rest
   if (i < K && j == 0) jstar[(size_t)bt * K + i] = jd;
 }
 
-template <int DT>
+// MODE kFinTable: walk the decided table (jstar, qtab); kFinMaxSum: qtab is
+// the pair scores S and the block finds the max-sum path (jstar unused)
+template <int DT, int MODE>
 __global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
     const void* __restrict__ Z, int L, int V, int K, int n_chunk, const float* __restrict__ T,
     const uint64_t* __restrict__ seed, uint64_t cycle, const int32_t* __restrict__ cand_idx,
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
     int32_t* __restrict__ draft_tok, float* __restrict__ q, const ChunkStat* __restrict__ stats,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
   __shared__ FinLds f;
-  finalize_stream<DT, true>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, jstar, qtab,
+  finalize_stream<DT, MODE>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, jstar, qtab,
                             path_rank, draft_tok, q, stats, accept_len, out_tok);
 }
 
@@ -240,18 +243,22 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
 }
 
 hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
-                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws, const float* S_maxsum,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
                                  int32_t* out_tok, hipStream_t st) {
   const dim3 grid((unsigned)d.B);
   const float* zc = reinterpret_cast<const float*>(ws + w.zc);
   const int32_t* jstar = reinterpret_cast<const int32_t*>(ws + w.jstar);
-  const float* qtab = reinterpret_cast<const float*>(ws + w.qtab);
+  const float* qtab = S_maxsum ? S_maxsum : reinterpret_cast<const float*>(ws + w.qtab);
   const ChunkStat* stats = reinterpret_cast<const ChunkStat*>(ws + w.stats);
-#define DF_FIN(DT)                                                                                             \
-  launch(trace_finalize_kernel<DT>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K, w.n_chunk, T, seed, cycle, \
-         cand_idx, zc, jstar, qtab, path_rank, draft_tok, q, stats, accept_len, out_tok)
-  if (d.logit_dtype == DFLASH_BF16) DF_FIN(DFLASH_BF16); else DF_FIN(DFLASH_F32);
+#define DF_FIN(DT, MODE)                                                                                        \
+  launch(trace_finalize_kernel<DT, MODE>, grid, dim3(kFinThreads), st, Z, d.L, d.V, d.K, w.n_chunk, T, seed,   \
+         cycle, cand_idx, zc, jstar, qtab, path_rank, draft_tok, q, stats, accept_len, out_tok)
+  if (S_maxsum) {
+    if (d.logit_dtype == DFLASH_BF16) DF_FIN(DFLASH_BF16, kFinMaxSum); else DF_FIN(DFLASH_F32, kFinMaxSum);
+  } else {
+    if (d.logit_dtype == DFLASH_BF16) DF_FIN(DFLASH_BF16, kFinTable); else DF_FIN(DFLASH_F32, kFinTable);
+  }
 #undef DF_FIN
   return hipGetLastError();
 }

@@ -98,7 +98,7 @@ hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const in
                                const void* Z, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
                                int32_t* cand_idx, float* cand_logit, float* S, hipStream_t st);
 hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
-                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
+                                 const float* T, const uint64_t* seed, uint64_t cycle, char* ws, const float* S_maxsum,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
                                  int32_t* out_tok, hipStream_t st);
 hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, const void* Wt, float* y,

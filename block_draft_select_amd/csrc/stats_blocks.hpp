@@ -316,21 +316,30 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
   return n_item - 1;
 }
 
-// q of position t (t < L, K values in LDS): with the trace, the table row of
-// its predecessor's rank (rank 0 at t = 0); else the q the caller passed
-template <bool WITH_TRACE>
+// What the finalize block does besides the verify: nothing (path_rank and q
+// are inputs), the walk over the decided trace table, or the max-sum trace
+// over the pair scores
+enum { kFinVerify = 0, kFinTable = 1, kFinMaxSum = 2 };
+
+// q of position t (t < L, K values in LDS): with the table walk, the table
+// row of its predecessor's rank (rank 0 at t = 0); else the q in f.qs (the
+// caller's, or one-hot at the max-sum path)
+template <bool TABLE>
 __device__ __forceinline__ const float* q_row_of(const FinLds& f, int t, int K) {
-  if (WITH_TRACE) return &f.S[(t * K + (t > 0 ? f.rank[t - 1] : 0)) * K];
+  if (TABLE) return &f.S[(t * K + (t > 0 ? f.rank[t - 1] : 0)) * K];
   return f.qs[t];
 }
 
-// One block per stream.  WITH_TRACE: the block also walks the trace over
-// the decided trace table (jstar: decision of every row (t, i); qtab: the
-// q of every row, [B, L, K, K]) and writes path_rank / draft_tok / q;
-// otherwise path_rank and q are inputs.  With WITH_TRACE, zc_pre holds the
-// candidates' target logits [B, L, K] (fp32-exact values); otherwise it is
-// not read and they are gathered here.
-template <int DT, bool WITH_TRACE>
+// One block per stream.  MODE kFinTable: the block also walks the trace
+// over the decided trace table (jstar: decision of every row (t, i); qtab:
+// the q of every row, [B, L, K, K]) and writes path_rank / draft_tok / q.
+// kFinMaxSum: qtab holds the pair scores S [B, L, K, K]; wave 0 finds the
+// max-sum path (the dynamic programme of dflash_trace_viterbi, the same
+// arithmetic in the same order) and writes path_rank / draft_tok and a
+// one-hot q.  kFinVerify: path_rank and q are inputs.  In the first two
+// modes zc_pre holds the candidates' target logits [B, L, K] (fp32-exact
+// values); otherwise it is not read and they are gathered here.
+template <int DT, int MODE>
 __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, int L, int V, int K, int n_chunk,
                                 const float* __restrict__ T, const uint64_t* __restrict__ seed, uint64_t cycle,
                                 const int32_t* __restrict__ cand_idx, const float* __restrict__ zc_pre,
@@ -361,18 +370,18 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   const int ci_raw = cand_idx[e0 + ei];
   // with the trace (the fused cycle) the scores launch has gathered the
   // candidates' target logits into zc_pre; the split verify reads them from Z
-  const float zc_raw = WITH_TRACE ? zc_pre[e0 + ei] : 0.f;
-  const float q_raw = WITH_TRACE ? 0.f : q[e0 + ei];
-  const int pr_raw = WITH_TRACE ? 0 : path_rank[(size_t)b * L + min(tid, L - 1)];
+  const float zc_raw = MODE != kFinVerify ? zc_pre[e0 + ei] : 0.f;
+  const float q_raw = MODE == kFinVerify ? q[e0 + ei] : 0.f;
+  const int pr_raw = MODE == kFinVerify ? path_rank[(size_t)b * L + min(tid, L - 1)] : 0;
   constexpr int NS = DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX / kFinThreads;
   const size_t s0 = (size_t)b * lk * K;
   const int n = lk * K;
   float sv[NS];
   int js = 0;
-  if (WITH_TRACE) {
+  if (MODE != kFinVerify) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) sv[k] = qtab[s0 + min(tid + k * kFinThreads, n - 1)];
-    js = jstar[e0 + ei];
+    if (MODE == kFinTable) js = jstar[e0 + ei];
   }
   constexpr int NC = kTermCache / kFinThreads;
   float2 mv[NC];
@@ -389,15 +398,15 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     const int t = tid / K, k = tid - (tid / K) * K;
     const int ci = clamp_idx(ci_raw, V);
     f.cand[t][k] = ci;
-    if (!WITH_TRACE) f.qs[t][k] = q_raw;
-    if (!greedy) f.zc[t][k] = WITH_TRACE ? (double)zc_raw : logit_at<DT>(Z, (zrow0 + t) * Vs + ci);
+    if (MODE == kFinVerify) f.qs[t][k] = q_raw;
+    if (!greedy) f.zc[t][k] = MODE != kFinVerify ? (double)zc_raw : logit_at<DT>(Z, (zrow0 + t) * Vs + ci);
   }
-  if (!WITH_TRACE && tid < L) f.rank[tid] = clamp_idx(pr_raw, K);
-  if (WITH_TRACE) {
+  if (MODE == kFinVerify && tid < L) f.rank[tid] = clamp_idx(pr_raw, K);
+  if (MODE != kFinVerify) {
 #pragma unroll
     for (int k = 0; k < NS; ++k)
       if (tid + k * kFinThreads < n) f.S[tid + k * kFinThreads] = sv[k];
-    if (tid < lk) f.jstar[tid] = min(max(js, 0), K - 1);
+    if (MODE == kFinTable && tid < lk) f.jstar[tid] = min(max(js, 0), K - 1);
   }
   if (cached) {
 #pragma unroll
@@ -410,7 +419,60 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   // target row; with the trace, wave 0 meanwhile walks the decided table
   // from rank 0 (L look-ups) and copies out each position's q (the row of
   // its predecessor's rank), rank and token
-  if (WITH_TRACE && wave == 0) {
+  if (MODE == kFinMaxSum && wave == 0) {
+    // the max-sum path over the scores in f.S: lane j < K holds best_t(j),
+    // predecessor values come by lane reads, 4-bit back pointers of steps
+    // 0..7 and 8..15 in two registers; first index at every tie
+    const bool live = lane < K;
+    const int jr = min(lane, K - 1);
+    double best = live ? (double)f.S[jr] : -INFINITY;
+    uint32_t bk0 = 0, bk1 = 0;
+#pragma unroll 1
+    for (int t = 1; t < L; ++t) {
+      const int hi = __double2hiint(best), lo = __double2loint(best);
+      const float* col = &f.S[t * K * K + jr];  // rows past K stay inside f.S and are ignored
+      float ev[DFLASH_K_MAX];
+#pragma unroll
+      for (int i = 0; i < DFLASH_K_MAX; ++i) ev[i] = col[i * K];
+      double m = -INFINITY;
+      int arg = 0;
+#pragma unroll
+      for (int i = 0; i < DFLASH_K_MAX; ++i) {
+        const double v =
+            __hiloint2double(__builtin_amdgcn_readlane(hi, i), __builtin_amdgcn_readlane(lo, i)) + (double)ev[i];
+        if (i < K && v > m) {
+          m = v;
+          arg = i;
+        }
+      }
+      if (live) {
+        best = m;
+        if (t < 8) bk0 |= (uint32_t)arg << (4 * t);
+        else bk1 |= (uint32_t)arg << (4 * (t - 8));
+      }
+    }
+    double mx = best;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    const unsigned long long hit = __ballot(live && best == mx);
+    int jc = hit ? __ffsll((long long)hit) - 1 : 0;
+    int mine = lane == L - 1 ? jc : 0;
+#pragma unroll 1
+    for (int t = L - 1; t >= 1; --t) {
+      const uint32_t wv = __builtin_amdgcn_readlane(t < 8 ? bk0 : bk1, jc);
+      jc = (int)((wv >> (4 * (t & 7))) & 15u);
+      if (lane == t - 1) mine = jc;
+    }
+    if (lane < L) {
+      f.rank[lane] = mine;
+      path_rank[(size_t)b * L + lane] = mine;
+      draft_tok[(size_t)b * L + lane] = f.cand[lane][mine];
+    }
+    for (int i = lane; i < L * K; i += kWave) {
+      const int t = i / K;
+      f.qs[t][i - t * K] = i - t * K == __shfl(mine, t) ? 1.f : 0.f;
+    }
+  } else if (MODE == kFinTable && wave == 0) {
     // the table's decisions in registers (lane l holds rows l, l + 64, ...)
     // so that each step of the chain is a lane read, not an LDS round trip
     constexpr int NJ = DFLASH_L_MAX * DFLASH_K_MAX / kWave;
@@ -436,18 +498,19 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       draft_tok[(size_t)b * L + lane] = f.cand[lane][mine];
     }
   } else {
-    constexpr int w0 = WITH_TRACE ? 1 : 0;
+    constexpr int w0 = MODE != kFinVerify ? 1 : 0;
     for (int t = wave - w0; t <= L; t += kFinWaves - w0)
       combine_row<DT>(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, greedy, invT, lane);
   }
   __syncthreads();
 
-  // the q output of the trace: the row of each position's predecessor's
-  // rank, written by the last wave (idle or nearly so in the next phase)
-  if (WITH_TRACE && wave == kFinWaves - 1) {
+  // the q output of the trace (the row of each position's predecessor's
+  // rank, or one-hot at the max-sum path), written by the last wave (idle
+  // or nearly so in the next phase)
+  if (MODE != kFinVerify && wave == kFinWaves - 1) {
     for (int i = lane; i < L * K; i += kWave) {
       const int t = i / K;
-      q[(size_t)b * L * K + i] = q_row_of<WITH_TRACE>(f, t, K)[i - t * K];
+      q[(size_t)b * L * K + i] = q_row_of<MODE == kFinTable>(f, t, K)[i - t * K];
     }
   }
   const size_t o = (size_t)b * (L + 1);
@@ -470,14 +533,14 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
       const int j = f.rank[lane];
       const double u = (double)u01_f32(f.rnd0[lane].y);
       const double p = f.pc[lane][j] / f.rowAll[lane];
-      rejected = !(u * (double)q_row_of<WITH_TRACE>(f, lane, K)[j] < p);
+      rejected = !(u * (double)q_row_of<MODE == kFinTable>(f, lane, K)[j] < p);
     }
     const int fl = first_lane(rejected);
     if (lane == 0) f.s_n = fl < L ? fl : L;
   } else {
     for (int t = wave - 1; t <= L; t += kFinWaves - 1) {
       const int pk = pick_item(f, st_all + (size_t)t * n_chunk, t, L, K, n_chunk, cached, invT,
-                               t < L ? q_row_of<WITH_TRACE>(f, t, K) : f.qs[0], lane);
+                               t < L ? q_row_of<MODE == kFinTable>(f, t, K) : f.qs[0], lane);
       if (lane == 0) f.pick_row[t] = pk;
     }
   }

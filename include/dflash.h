@@ -182,12 +182,12 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* The whole cycle with the max-sum trace (dflash_trace_viterbi) in place of
- * the greedy/sampled walk: the streaming launch and the candidate/score
- * launch of dflash_cycle, then the max-sum trace, then the verify of
- * dflash_verify's finalize on the chunk statistics the streaming launch
- * wrote.  Same arguments, layouts and workspace as dflash_cycle; q is
- * one-hot.  Outputs equal those of dflash_topk, dflash_pair_scores,
- * dflash_trace_viterbi and dflash_verify called in turn. */
+ * the greedy/sampled walk, in three launches like dflash_cycle: its
+ * streaming and candidate/score launches, then one block per stream that
+ * finds the max-sum path over the pair scores and runs the verify.  Same
+ * arguments, layouts and workspace as dflash_cycle; q is one-hot.  Outputs
+ * equal those of dflash_topk, dflash_pair_scores, dflash_trace_viterbi and
+ * dflash_verify called in turn. */
 dflash_status dflash_cycle_maxsum(const dflash_dims* d, const void* U, const void* Z,
                                   const int32_t* x0, const void* E, const void* W_g, const void* h,
                                   const float* T, const uint64_t* seed, uint64_t cycle,
