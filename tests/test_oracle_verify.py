@@ -112,6 +112,40 @@ def test_emitted_tokens_follow_target(V, K, L, T, chunk):
         assert _chi2_pvalue(np.array(emitted[t]), p) > 1e-4, f"position {t + 1}"
 
 
+@pytest.mark.parametrize("V,K,L,T,chunk", [
+    (8, 2, 2, 1.0, 4096),
+    (16, 4, 3, 0.7, 5),
+    (64, 16, 2, 1.3, 16),
+])
+def test_one_hot_max_sum_proposal_keeps_target_law(V, K, L, T, chunk):
+    # the max-sum path is deterministic, so its q is one-hot; the accept test
+    # is then u < p(d) and the residual is p without d: the emitted token at
+    # every position must still follow p, and position 1 is accepted with
+    # probability sum(min(p, q)) = p(d_1)
+    from oracle import viterbi
+    rng = np.random.default_rng(V * 1000 + K + 7)
+    Z, S, cand = _tiny_stream(rng, L, V, K)
+    path, draft, _, _ = viterbi.viterbi_stream(S, cand)
+    q = np.zeros((L, K))
+    q[np.arange(L), path] = 1.0
+    n_cycles = 6000
+    emitted = [[] for _ in range(L + 1)]
+    acc1 = 0
+    for c in range(n_cycles):
+        n, out, _ = dflash.verify_stream(Z, cand, path, q, T, 0x777 + V, c, chunk=chunk)
+        for t in range(n + 1):
+            emitted[t].append(int(out[t]))
+        acc1 += n >= 1
+    for t in range(L + 1):
+        if len(emitted[t]) < 200:
+            continue
+        pt = special.softmax(Z[t] / T)
+        assert _chi2_pvalue(np.array(emitted[t]), pt) > 1e-4, f"position {t + 1}"
+    p1 = special.softmax(Z[0] / T)[int(draft[0])]
+    sd = np.sqrt(p1 * (1 - p1) / n_cycles)
+    assert abs(acc1 / n_cycles - p1) < 5 * sd + 1e-12
+
+
 def test_first_position_acceptance_closed_form():
     rng = np.random.default_rng(77)
     V, K, L, T = 10, 3, 1, 1.0
