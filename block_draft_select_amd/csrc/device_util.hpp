@@ -279,4 +279,35 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// One step of the max-sum dynamic programme for lane j: over predecessors
+// i < K, the maximum of best(i) + col[i * K] and the first i attaining it.
+// best(i) is lane i's value of `best` (lane reads); col[i * K] must be
+// readable for every i < 16 (rows past K are read and ignored).  The
+// comparisons form a 4-level tree that keeps the lower index on ties, so
+// the result is the same as a left-to-right scan with a strict compare.
+__device__ __forceinline__ void maxplus_step(double best, const float* col, int K, double& m_out, int& arg_out) {
+  const int hi = __double2hiint(best), lo = __double2loint(best);
+  float ev[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ev[i] = col[i * K];
+  double v[16];
+  int a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const double pv = __hiloint2double(__builtin_amdgcn_readlane(hi, i), __builtin_amdgcn_readlane(lo, i));
+    v[i] = i < K ? pv + (double)ev[i] : -INFINITY;
+    a[i] = i;
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * w) {
+      const bool right = v[i + w] > v[i];  // ties keep the lower index
+      v[i] = right ? v[i + w] : v[i];
+      a[i] = right ? a[i + w] : a[i];
+    }
+  m_out = v[0];
+  arg_out = a[0];
+}
+
 }  // namespace dfk

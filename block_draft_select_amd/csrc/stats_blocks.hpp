@@ -429,22 +429,9 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     uint32_t bk0 = 0, bk1 = 0;
 #pragma unroll 1
     for (int t = 1; t < L; ++t) {
-      const int hi = __double2hiint(best), lo = __double2loint(best);
-      const float* col = &f.S[t * K * K + jr];  // rows past K stay inside f.S and are ignored
-      float ev[DFLASH_K_MAX];
-#pragma unroll
-      for (int i = 0; i < DFLASH_K_MAX; ++i) ev[i] = col[i * K];
-      double m = -INFINITY;
-      int arg = 0;
-#pragma unroll
-      for (int i = 0; i < DFLASH_K_MAX; ++i) {
-        const double v =
-            __hiloint2double(__builtin_amdgcn_readlane(hi, i), __builtin_amdgcn_readlane(lo, i)) + (double)ev[i];
-        if (i < K && v > m) {
-          m = v;
-          arg = i;
-        }
-      }
+      double m;
+      int arg;
+      maxplus_step(best, &f.S[t * K * K + jr], K, m, arg);  // rows past K stay inside f.S
       if (live) {
         best = m;
         if (t < 8) bk0 |= (uint32_t)arg << (4 * t);

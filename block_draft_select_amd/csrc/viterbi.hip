@@ -42,34 +42,22 @@ __global__ __launch_bounds__(64) void viterbi_kernel(const float* __restrict__ S
   for (int u = 0; u < DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX / 64; ++u) Ss[u * 64 + lane] = v[u];
   __syncthreads();
 
-  // the loops below stay rolled: one wave per CU runs this code once, so its
-  // length costs instruction fetches.  Lane j < K holds best_t(j); its back
-  // pointers are 4-bit fields, steps
-  // 0..7 in bk0 and 8..15 in bk1
+  // the step loops stay rolled (one wave issues every instruction of the
+  // body itself, so a fully unrolled body measured slower).  Lane j < K
+  // holds best_t(j); its back pointers are 4-bit fields, steps 0..7 in bk0
+  // and 8..15 in bk1
   const bool live = lane < K;
   const int jr = min(lane, K - 1);  // lanes past K read a valid column and discard it
   double best = live ? (double)Ss[jr] : -INFINITY;
   uint32_t bk0 = 0, bk1 = 0;
 #pragma unroll 1
   for (int t = 1; t < L; ++t) {
-    // predecessor values best_{t-1}(i) from lane i (lane reads, no LDS round trip)
-    const int hi = __double2hiint(best), lo = __double2loint(best);
-    const float* col = &Ss[t * K * K + jr];  // S[t][i][j] at col[i * K]
-    // all 16 column reads issued together (rows past K stay inside the
-    // buffer: (L-1)K^2 + K - 1 + 15K < 4096) and ignored in the compare
-    float ev[DFLASH_K_MAX];
-#pragma unroll
-    for (int i = 0; i < DFLASH_K_MAX; ++i) ev[i] = col[i * K];
-    double m = -INFINITY;
-    int arg = 0;
-#pragma unroll
-    for (int i = 0; i < DFLASH_K_MAX; ++i) {
-      const double v = __hiloint2double(__builtin_amdgcn_readlane(hi, i), __builtin_amdgcn_readlane(lo, i)) + (double)ev[i];
-      if (i < K && v > m) {
-        m = v;
-        arg = i;
-      }
-    }
+    // predecessor values best_{t-1}(i) from lane i (lane reads, no LDS
+    // round trip); all 16 column reads issued together (rows past K stay
+    // inside the buffer: (L-1)K^2 + K - 1 + 15K < 4096) and ignored
+    double m;
+    int arg;
+    maxplus_step(best, &Ss[t * K * K + jr], K, m, arg);
     if (live) {
       best = m;
       if (t < 8) bk0 |= (uint32_t)arg << (4 * t);
