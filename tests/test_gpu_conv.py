@@ -74,6 +74,13 @@ CASES = [
     ("f32-ragged", 1, dict(B=3, L=4, hidden=80), None),
     ("bf16-concurrent-32", 3, dict(), None),                       # B 32, L 8, hidden 2048
     ("bf16-large-vocab-128", 5, dict(), [0, 77, 127]),              # B 128, L 8, hidden 3072
+    # limits: one row at the smallest hidden; a wide hidden on the small
+    # tiles; the large tiles with ragged rows (500 = 3 * 128 + 116), ragged
+    # channels (4112 = 64 * 64 + 16) and an odd stage count (one stage of
+    # loads in flight)
+    ("bf16-one-row-min-hidden", 3, dict(B=1, L=1, hidden=16), None),
+    ("bf16-wide-hidden", 3, dict(B=2, L=2, hidden=4096), None),
+    ("bf16-large-tiles-ragged", 3, dict(B=100, L=5, hidden=4112), [0, 51, 99]),
 ]
 
 

@@ -110,6 +110,10 @@ CASES = [
     ("K1-L1", 3, dict(B=2, V=1000, hidden=256, K=1, L=1), None),
     ("L2-mixedT", 5, dict(B=6, V=12296, hidden=512, L=2, e_std=0.3), None),
     ("concurrent-32", 3, dict(), [0, 13, 31]),
+    # limits: every token a candidate (the residual has no chunk mass); the
+    # largest row count B (L + 1) = 65535
+    ("V-eq-K", 3, dict(B=3, V=16, K=16, hidden=256, plant=None, e_std=0.3), None),
+    ("max-rows", 3, dict(B=3855, L=16, V=64, hidden=16, r=16, plant=None), [0, 1927, 3854]),
 ]
 
 
