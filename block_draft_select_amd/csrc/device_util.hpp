@@ -279,35 +279,48 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// One step of the max-sum dynamic programme for lane j: over predecessors
-// i < K, the maximum of best(i) + col[i * K] and the first i attaining it.
-// best(i) is lane i's value of `best` (lane reads); col[i * K] must be
-// readable for every i < 16 (rows past K are read and ignored).  The
-// comparisons form a 4-level tree that keeps the lower index on ties, so
-// the result is the same as a left-to-right scan with a strict compare.
-__device__ __forceinline__ void maxplus_step(double best, const float* col, int K, double& m_out, int& arg_out) {
-  const int hi = __double2hiint(best), lo = __double2loint(best);
-  float ev[16];
+// One step of the max-sum dynamic programme on a whole wave: lane
+// g * 16 + j (g = 0..3) takes predecessors i = 4g .. 4g + 3 of successor j,
+// so every lane must hold best(j) of its column j = lane % 16 on entry (the
+// four groups are replicas).  On exit every lane holds, for its column, the
+// maximum over i < K of best(i) + St[i * K + j] and the first i attaining
+// it.  St is the step's K x K score block; rows and columns past K are read
+// clamped and ignored.  The local pairs and the two cross-group rounds keep
+// the lower index on ties, so the result equals a left-to-right scan with a
+// strict compare.
+__device__ __forceinline__ void maxplus_step(double best, const float* St, int K, int lane, double& m_out,
+                                             int& arg_out) {
+  const int j = min(lane & 15, K - 1), g = lane >> 4;
+  double v[4];
+  int a[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) ev[i] = col[i * K];
-  double v[16];
-  int a[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const double pv = __hiloint2double(__builtin_amdgcn_readlane(hi, i), __builtin_amdgcn_readlane(lo, i));
-    v[i] = i < K ? pv + (double)ev[i] : -INFINITY;
-    a[i] = i;
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * g + u;
+    const double pv = __shfl(best, (lane & 48) | i);  // best(i), from lane i of this group
+    const float ev = St[min(i, K - 1) * K + j];
+    v[u] = i < K ? pv + (double)ev : -INFINITY;
+    a[u] = i;
   }
 #pragma unroll
-  for (int w = 1; w < 16; w *= 2)
+  for (int w = 1; w < 4; w *= 2)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2 * w) {
-      const bool right = v[i + w] > v[i];  // ties keep the lower index
-      v[i] = right ? v[i + w] : v[i];
-      a[i] = right ? a[i + w] : a[i];
+    for (int u = 0; u < 4; u += 2 * w) {
+      const bool right = v[u + w] > v[u];  // ties keep the lower index
+      v[u] = right ? v[u + w] : v[u];
+      a[u] = right ? a[u + w] : a[u];
     }
-  m_out = v[0];
-  arg_out = a[0];
+  double m = v[0];
+  int arg = a[0];
+#pragma unroll
+  for (int off = 16; off <= 32; off *= 2) {
+    const double mp = __shfl_xor(m, off);
+    const int ap = __shfl_xor(arg, off);
+    const bool take = mp > m || (mp == m && ap < arg);
+    m = take ? mp : m;
+    arg = take ? ap : arg;
+  }
+  m_out = m;
+  arg_out = arg;
 }
 
 }  // namespace dfk

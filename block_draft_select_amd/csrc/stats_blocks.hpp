@@ -420,18 +420,19 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   // from rank 0 (L look-ups) and copies out each position's q (the row of
   // its predecessor's rank), rank and token
   if (MODE == kFinMaxSum && wave == 0) {
-    // the max-sum path over the scores in f.S: lane j < K holds best_t(j),
-    // predecessor values come by lane reads, 4-bit back pointers of steps
-    // 0..7 and 8..15 in two registers; first index at every tie
-    const bool live = lane < K;
-    const int jr = min(lane, K - 1);
+    // the max-sum path over the scores in f.S: lane g * 16 + j holds
+    // best_t(j) (four replicas), a step splits the predecessors across the
+    // groups, 4-bit back pointers of steps 0..7 and 8..15 in two registers;
+    // first index at every tie
+    const bool live = (lane & 15) < K;  // four 16-lane replicas of the columns
+    const int jr = min(lane & 15, K - 1);
     double best = live ? (double)f.S[jr] : -INFINITY;
     uint32_t bk0 = 0, bk1 = 0;
 #pragma unroll 1
     for (int t = 1; t < L; ++t) {
       double m;
       int arg;
-      maxplus_step(best, &f.S[t * K * K + jr], K, m, arg);  // rows past K stay inside f.S
+      maxplus_step(best, &f.S[t * K * K], K, lane, m, arg);
       if (live) {
         best = m;
         if (t < 8) bk0 |= (uint32_t)arg << (4 * t);

@@ -14,9 +14,10 @@
 // deterministic, so q is one-hot at each chosen rank.
 //
 // One wave per stream: the stream's scores go to LDS with coalesced loads,
-// lane j holds best_t(j) and its 4-bit back pointers in two registers, each
-// DP step takes the K predecessor values by lane reads (no LDS round trip,
-// no barrier), and the backtrack is L lane reads of uniform indices.
+// the four 16-lane groups each hold best_t(j) of every column j and its
+// 4-bit back pointers in two registers, a DP step splits the predecessors
+// four ways across the groups (lane shuffles, no barrier), and the backtrack
+// is L lane reads of uniform indices.
 #include "device_util.hpp"
 #include "internal.hpp"
 
@@ -43,21 +44,19 @@ __global__ __launch_bounds__(64) void viterbi_kernel(const float* __restrict__ S
   __syncthreads();
 
   // the step loops stay rolled (one wave issues every instruction of the
-  // body itself, so a fully unrolled body measured slower).  Lane j < K
-  // holds best_t(j); its back pointers are 4-bit fields, steps 0..7 in bk0
-  // and 8..15 in bk1
-  const bool live = lane < K;
-  const int jr = min(lane, K - 1);  // lanes past K read a valid column and discard it
+  // body itself, so a fully unrolled body measured slower).  Lane
+  // g * 16 + j holds best_t(j) of column j = lane % 16 < K (four replicas);
+  // its back pointers are 4-bit fields, steps 0..7 in bk0 and 8..15 in bk1
+  const bool live = (lane & 15) < K;
+  const int jr = min(lane & 15, K - 1);  // lanes past K read a valid column and discard it
   double best = live ? (double)Ss[jr] : -INFINITY;
   uint32_t bk0 = 0, bk1 = 0;
 #pragma unroll 1
   for (int t = 1; t < L; ++t) {
-    // predecessor values best_{t-1}(i) from lane i (lane reads, no LDS
-    // round trip); all 16 column reads issued together (rows past K stay
-    // inside the buffer: (L-1)K^2 + K - 1 + 15K < 4096) and ignored
+    // the step over all 64 lanes (predecessor values by lane shuffles)
     double m;
     int arg;
-    maxplus_step(best, &Ss[t * K * K + jr], K, m, arg);
+    maxplus_step(best, &Ss[t * K * K], K, lane, m, arg);
     if (live) {
       best = m;
       if (t < 8) bk0 |= (uint32_t)arg << (4 * t);
