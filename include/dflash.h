@@ -5,7 +5,8 @@
  * The method (four web pages on DFlash 2, cited by title and section):
  *   P1 "DFlash 2: Block diffusion, wearing a drafter's coat", section
  *      "The architecture" (sub-sections "Sixteen candidates per position",
- *      "A path selector", "Lossless, with conditions I did not used to state").
+ *      "A path selector", "Suffix-decay convolution", "Lossless, with
+ *      conditions I did not used to state").
  *   P2 "A 2B Drafter Made a 27B Model 3.4x Faster. Same Exact Output.",
  *      sections "What a block-diffusion drafter is, and why it kept
  *      breaking", "The two fixes", "Caveats before you rebuild your serving
@@ -20,6 +21,12 @@
  * through the candidate lattice, and verifies it against L+1 target logit
  * rows Z by rejection sampling (accept with min(1, p/q), resample from the
  * normalised residual max(0, p - q), bonus token when all L are accepted).
+ * dflash_cycle does the whole cycle in three launches; dflash_topk,
+ * dflash_pair_scores, dflash_trace and dflash_verify are its steps one by
+ * one.  Beside them: dflash_trace_viterbi and dflash_cycle_maxsum take the
+ * path of largest summed score instead of the greedy/sampled walk, and
+ * dflash_conv2tap is the drafter's two-tap dynamic convolution, upstream of
+ * the context vectors h.
  *
  * Conventions for every entry point:
  *   - Every array argument is a DEVICE pointer owned by the caller; the
