@@ -22,7 +22,7 @@ K_MAX, L_MAX, R_MAX, V_MAX, CHUNK = 16, 16, 256, 2097152, 4096
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 KERNELS = ("topk", "gate", "scores", "trace", "stats", "finalize", "cycle_stream", "cycle_scores",
-           "cycle_finalize", "conv2tap", "trace_viterbi")
+           "cycle_finalize", "conv2tap", "trace_viterbi", "topk_merge")
 
 
 class dflash_dims(ctypes.Structure):
@@ -59,6 +59,7 @@ def _load():
         "dflash_cycle_maxsum": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dflash_conv2tap": (I32, [D, P, P, P, P, P]),
         "dflash_trace_viterbi": (I32, [D, P, P, P, P, P, P]),
+        "dflash_topk_merge": (I32, [D, I32, ctypes.POINTER(I32), P, P, P, P, P]),
         "dflash_read_probe": (I32, [P, SZ, P, P]),
         "dflash_copy_probe": (I32, [P, P, SZ, P]),
         "dflash_kernel_name": (ctypes.c_char_p, [I32]),
@@ -204,6 +205,17 @@ def dflash_cycle_maxsum(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_
                         stream=None):
     _cycle_call(lib.dflash_cycle_maxsum, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
                 cand_idx, cand_logit, S, path_rank, draft_tok, q, stream)
+
+
+def dflash_topk_merge(d, shard_begin, cand_idx_parts, cand_logit_parts, cand_idx, cand_logit, stream=None):
+    """``shard_begin``: a Python sequence of the shards' first token indices."""
+    R, n = d.B * d.L, len(shard_begin)
+    begins = (ctypes.c_int32 * n)(*[int(v) for v in shard_begin])
+    _check(lib.dflash_topk_merge(ctypes.byref(d), n, begins,
+                                 _ptr(cand_idx_parts, "cand_idx_parts", torch.int32, n * R * d.K),
+                                 _ptr(cand_logit_parts, "cand_logit_parts", torch.float32, n * R * d.K),
+                                 _ptr(cand_idx, "cand_idx", torch.int32, R * d.K),
+                                 _ptr(cand_logit, "cand_logit", torch.float32, R * d.K), _stream(stream)))
 
 
 def dflash_trace_viterbi(d, S, cand_idx, path_rank, draft_tok, q, stream=None):

@@ -292,6 +292,34 @@ dflash_status dflash_trace(const dflash_dims* d, const float* S, const int32_t* 
   }
 }
 
+dflash_status dflash_topk_merge(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                const int32_t* cand_idx_parts, const float* cand_logit_parts, int32_t* cand_idx,
+                                float* cand_logit, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (n_shards < 1 || n_shards > DFLASH_MAX_SHARDS)
+      return fail(DFLASH_ERR_INVALID_ARG, "n_shards must be in 1 .. DFLASH_MAX_SHARDS");
+    if (!shard_begin) return fail(DFLASH_ERR_INVALID_ARG, "shard_begin is NULL");
+    if (dflash_status s = check_ptrs({{cand_idx_parts, "cand_idx_parts", false},
+                                      {cand_logit_parts, "cand_logit_parts", false},
+                                      {cand_idx, "cand_idx", false}, {cand_logit, "cand_logit", false}})) return s;
+    dfk::ShardBegins sb{};
+    for (int s = 0; s < n_shards; ++s) {
+      const int64_t lo = shard_begin[s], hi = s + 1 < n_shards ? shard_begin[s + 1] : d->V;
+      if ((s == 0 && lo != 0) || hi - lo < d->K || hi > d->V)
+        return fail(DFLASH_ERR_INVALID_ARG, "shards must start at 0, increase, and be at least K tokens wide");
+      sb.begin[s] = (int32_t)lo;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_TOPK_MERGE, st, [&] {
+      return dfk::launch_topk_merge(*d, n_shards, sb, cand_idx_parts, cand_logit_parts, cand_idx, cand_logit, st);
+    }), "top-K merge launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
 dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
                                    int32_t* draft_tok, float* q, void* stream) {
   try {
@@ -429,7 +457,7 @@ dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* 
 const char* dflash_kernel_name(int32_t kernel) {
   static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize",
                                                    "cycle_stream", "cycle_scores", "cycle_finalize", "conv2tap",
-                                                   "trace_viterbi"};
+                                                   "trace_viterbi", "topk_merge"};
   return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
 }
 

@@ -77,6 +77,12 @@ hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, flo
 hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t* cand_idx,
                          const float* cand_logit, const void* E, const float* gpart, float* S,
                          hipStream_t st);
+// first global token index of each vocabulary shard
+struct ShardBegins {
+  int32_t begin[DFLASH_MAX_SHARDS];
+};
+hipError_t launch_topk_merge(const dflash_dims& d, int n_shards, const ShardBegins& sb, const int32_t* idx_parts,
+                             const float* val_parts, int32_t* cand_idx, float* cand_logit, hipStream_t st);
 hipError_t launch_trace_viterbi(const dflash_dims& d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
                                 int32_t* draft_tok, float* q, hipStream_t st);
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,

@@ -67,6 +67,7 @@ extern "C" {
 #define DFLASH_ABI_VERSION 1
 #define DFLASH_K_MAX 16      /* candidates kept per position */
 #define DFLASH_L_MAX 16      /* drafted positions per block */
+#define DFLASH_MAX_SHARDS 64 /* vocabulary shards dflash_topk_merge combines */
 #define DFLASH_R_MAX 256     /* embedding rank */
 #define DFLASH_V_MAX 2097152 /* vocabulary size */
 #define DFLASH_CHUNK 4096    /* tokens per first-level item of the residual draw */
@@ -118,6 +119,27 @@ dflash_status dflash_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   cand_logit [B, L, K] float out: those logits, widened exactly to fp32 */
 dflash_status dflash_topk(const dflash_dims* d, const void* U, int32_t* cand_idx,
                           float* cand_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* S1 over a vocabulary split -- the exact top-K of every drafter row from
+ * the top-K lists of its vocabulary shards (P1 "Sixteen candidates per
+ * position": the K best tokens over the whole vocabulary).  Shard s covers
+ * tokens [shard_begin[s], shard_begin[s+1]) (the last one up to V); its list
+ * is what dflash_topk returns for the shard's own [B, L, width] slice of U
+ * (indices local to the shard).  The result equals dflash_topk over the whole
+ * of U: the K best of the union, value descending, then global index
+ * ascending, -0 equal to +0.
+ *   d                  B, L, V, K of the whole problem (validated as usual)
+ *   n_shards           1 .. DFLASH_MAX_SHARDS
+ *   shard_begin        HOST array [n_shards]: shard_begin[0] = 0, increasing,
+ *                      every shard at least K tokens wide
+ *   cand_idx_parts     [n_shards, B, L, K] int32, local indices in [0, width)
+ *   cand_logit_parts   [n_shards, B, L, K] float
+ *   cand_idx, cand_logit  [B, L, K] out (global indices)
+ * One launch on `stream` (one wave per row); no workspace.  Invalid
+ * arguments launch nothing and leave the outputs untouched. */
+dflash_status dflash_topk_merge(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                const int32_t* cand_idx_parts, const float* cand_logit_parts,
+                                int32_t* cand_idx, float* cand_logit, void* stream);
 
 /* S2 + S3 -- context gate and adjacent pair scores (P3 "A Lightweight Path
  * Selector"; P1 "A path selector").  With g_t[k] = sigmoid(sum_j
@@ -270,7 +292,8 @@ enum {
   DFLASH_KERNEL_CYCLE_FINALIZE = 8, /* dflash_cycle: trace + verify */
   DFLASH_KERNEL_CONV2TAP = 9,       /* dflash_conv2tap */
   DFLASH_KERNEL_TRACE_VITERBI = 10, /* dflash_trace_viterbi */
-  DFLASH_KERNEL_COUNT = 11
+  DFLASH_KERNEL_TOPK_MERGE = 11,    /* dflash_topk_merge */
+  DFLASH_KERNEL_COUNT = 12
 };
 
 /* Name of a kernel identifier ("" if out of range). */

@@ -104,6 +104,13 @@ def test_null_and_misaligned_pointers_rejected(dfl):
     assert dfl.lib.dflash_cycle_maxsum(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake, 0, fake,
                                        fake, None, None, None, None, None, None, fake, 1 << 30, None) == 1
     assert b"h is NULL" in dfl.lib.dflash_last_error()
+    begins = (ctypes.c_int32 * 2)(0, 2048)
+    assert dfl.lib.dflash_topk_merge(ctypes.byref(d), 2, begins, fake, fake, fake, None, None) == 1
+    assert b"cand_logit is NULL" in dfl.lib.dflash_last_error()
+    assert dfl.lib.dflash_topk_merge(ctypes.byref(d), 0, begins, fake, fake, fake, fake, None) == 1
+    bad_begins = (ctypes.c_int32 * 2)(0, 4094)  # last shard narrower than K
+    assert dfl.lib.dflash_topk_merge(ctypes.byref(d), 2, bad_begins, fake, fake, fake, fake, None) == 1
+    assert b"at least K" in dfl.lib.dflash_last_error()
     assert dfl.lib.dflash_trace_viterbi(ctypes.byref(d), fake, fake, fake, None, fake, None) == 1
     assert b"draft_tok is NULL" in dfl.lib.dflash_last_error()
     bad = dfl.dims(1, 17, 4096, 4, 16, 16, "bf16", "bf16")
