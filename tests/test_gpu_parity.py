@@ -61,6 +61,26 @@ def test_cycle_matches_oracle_small(name, cid, kw, gt):
         compare_stream(gpu, ref[b], b)
 
 
+# more seeded input sets of three representative shapes: sampling at T = 1
+# with a ragged vocabulary, mixed temperatures, a strong selector whose paths
+# leave top-1
+SEEDS = [(cid, kw, sid) for cid, kw in (
+    (3, dict(B=4, V=20008, hidden=256)),
+    (5, dict(B=6, V=12296, hidden=512)),
+    (3, dict(B=4, V=9000, hidden=256, e_std=0.3)),
+) for sid in (102, 103, 104, 105)]
+
+
+@pytest.mark.parametrize("cid,kw,sid", SEEDS, ids=[f"c{c[0]}-V{c[1]['V']}-set{c[2]}" for c in SEEDS])
+def test_cycle_matches_oracle_more_sets(cid, kw, sid):
+    inp = synth.make(cid, set_id=sid, **kw)
+    _say(f"[parity] set {sid}: config {cid} B={inp['B']} V={inp['V']}")
+    ref, _ = guarded(inp)
+    gpu = run_cycle(inp)
+    for b in range(inp["B"]):
+        compare_stream(gpu, ref[b], b)
+
+
 @pytest.mark.parametrize("ties", [False, True])
 def test_zero_embeddings_independent_top1(ties):
     inp = synth.make(3, set_id=5, B=4, V=8192, hidden=256, zero_E=True, ties=ties, T=0.0)
