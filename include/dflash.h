@@ -76,7 +76,7 @@ typedef int32_t dflash_status;
 enum {
   DFLASH_OK = 0,
   DFLASH_ERR_INVALID_ARG = 1, /* bad dimension, null or misaligned pointer */
-  DFLASH_ERR_UNSUPPORTED = 2, /* valid request this build does not handle */
+  DFLASH_ERR_UNSUPPORTED = 2, /* valid request the library does not handle */
   DFLASH_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   DFLASH_ERR_HIP = 4          /* the HIP runtime refused a launch */
 };

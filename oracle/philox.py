@@ -12,7 +12,7 @@ The pages on DFlash 2 name no generator at all; they only say the sampler
 preserves the target distribution (P1 "DFlash 2: Block diffusion, wearing a
 drafter's coat", section "Lossless, with conditions I did not used to state").
 A counter-based generator keyed by (stream seed) and indexed by (cycle,
-position, slot) is this build's reading: it makes every draw independent of
+position, slot) is a reading of the pages: it makes every draw independent of
 every decision ("non-anticipating"), and makes resuming at any cycle exact.
 
 Definition used here.  State: four 32-bit counter words x0..x3 and two 32-bit
