@@ -279,6 +279,20 @@ def main():
     mean_accept = float(out["accept_len"].float().mean().item())
     _log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/cycle")
 
+    # distribution of the cycle time: an event between consecutive cycles on
+    # the launching stream (a separate loop, so `value` stays a plain
+    # wall-clock throughput)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+    pct = lambda f: per[min(len(per) - 1, int(f * (len(per) - 1) + 0.5))]
+    cycle_us = {"p10": round(pct(0.1), 2), "median": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
+    _log(f"[bench] cycle time p10/median/p90 {cycle_us['p10']}/{cycle_us['median']}/{cycle_us['p90']} us")
+
     # per-kernel durations: HIP events recorded by the library around each
     # launch on the stream it launches on
     dfl.dflash_profile_enable(True)
@@ -367,6 +381,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "cycle_us": cycle_us,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
