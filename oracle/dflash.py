@@ -33,7 +33,9 @@ Readings of points the pages leave open:
              rejection draw from the normalised max(0, p - q) (candidates) /
              p (all other tokens); if all L are accepted, draw a bonus token
              from p_{L+1}; T = 0 replaces every draw by the argmax;
-  * one temperature per stream for both the selector and the target;
+  * one temperature per stream for both the selector and the target; a
+    stream samples when T > 0 and is greedy for every other value (0,
+    negative, NaN);
   * the residual draw is a two-level inverse CDF: first over items
              [chunk 0 .. chunk n_c-1, candidate 0 .. K-1] (chunks of CHUNK
              tokens in index order, carrying the non-candidate mass), then,
@@ -102,7 +104,8 @@ def gate(h_t, W):
 
 # --------------------------------------------------------------------------
 # S3: adjacent pair scores (P3 "A Lightweight Path Selector"; P1 "A path
-#     selector": low-rank bilinear attention over adjacent candidates)
+#     selector": neighbouring positions' candidates matched through a gated
+#     bilinear form of small rank)
 # --------------------------------------------------------------------------
 
 def pair_scores(pred_emb, cand_emb, cand_val, g):
@@ -145,9 +148,10 @@ def _cdf_margin(cum, j, target):
 
 
 # --------------------------------------------------------------------------
-# S4: trace (P3 "A Lightweight Path Selector": the only sequential part is a
-#     walk over the precomputed scores from the verified token; greedy
-#     follows the best successor, sampling draws from the scores)
+# S4: trace (P3 "A Lightweight Path Selector": once the scores exist, only
+#     a walk from the verified token is left in sequence; at T = 0 it takes
+#     the highest-scoring next candidate, at T > 0 it draws the next one
+#     from the scores)
 # --------------------------------------------------------------------------
 
 def trace_stream(S, cand_idx, T, seed, cycle):
@@ -157,8 +161,8 @@ def trace_stream(S, cand_idx, T, seed, cycle):
     rank), ``cand_idx`` is [L, K].  Row 0 is used at edge 1 (all rows of
     edge 1 are equal, its predecessor being x0).
 
-    T = 0: j_t = smallest rank attaining the maximum of S[t, j_{t-1}, :];
-           q_t is one-hot at j_t.
+    T <= 0 or NaN (greedy): j_t = smallest rank attaining the maximum of
+           S[t, j_{t-1}, :]; q_t is one-hot at j_t.
     T > 0: w = exp((row - max row) / T), q_t = w / sum(w); with u the fp32
            uniform from word 0 of the (seed; cycle, t, 0) Philox block,
            j_t = smallest rank whose cumulative weight exceeds u * total.
@@ -199,8 +203,9 @@ def trace_stream(S, cand_idx, T, seed, cycle):
 
 # --------------------------------------------------------------------------
 # S5 + S6: verify against the target (P1 "Lossless, with conditions ...":
-#     accept with probability min(1, p/q), otherwise resample from the
-#     residual; P2 "Caveats ...": greedy output equals the target's)
+#     a draft survives with chance min(1, p/q), and a rejected one is
+#     replaced by a draw from the residual; P2 "Caveats ...": greedy output
+#     equals the target's)
 # --------------------------------------------------------------------------
 
 def argmax_first(row):
@@ -223,8 +228,9 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
     ``path_rank`` [L], ``q`` [L, K] the drafting distribution over each
     position's candidates.
 
-    T = 0: a_t = argmax_first(Z_t); n = length of the longest prefix with
-           d_t == a_t; the emitted tokens are d_1..d_n, a_{n+1}.
+    T <= 0 or NaN (greedy): a_t = argmax_first(Z_t); n = length of the
+           longest prefix with d_t == a_t; the emitted tokens are
+           d_1..d_n, a_{n+1}.
     T > 0: p_t = softmax(Z_t / T).  Position t is accepted while
            u_t * q_t(d_t) < p_t(d_t), u_t the fp32 uniform from word 1 of
            the (seed; cycle, t, 0) block.  n = number accepted.  Row n+1 is
@@ -249,10 +255,9 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
     out = np.full(L + 1, -1, dtype=np.int64)
     margins = []
 
-    if T < 0 or not np.isfinite(T):
-        raise ValueError("temperature must be finite and >= 0")
-
-    if T == 0:
+    if not T > 0:
+        # greedy: T = 0 by the pages' convention, and by this build's reading
+        # every temperature that is not positive (negative or NaN) as well
         a = [argmax_first(Z[t]) for t in range(L + 1)]
         n = 0
         while n < L and draft[n] == a[n]:
