@@ -241,13 +241,15 @@ __device__ __forceinline__ int clamp_idx(int v, int n) { return v < 0 ? 0 : (v >
 // e^x for x <= 0 in fp64 (every exponent this library takes is a logit or
 // score minus a maximum, so never positive).  Cody & Waite reduction:
 // x = n ln2 + r with n = rint(x log2 e), |r| <= ln2 / 2, ln2 split into a
-// 12-bit head (n * head is exact) and a tail; e^r from its Taylor series to
-// degree 11 (truncation error below 1e-14 relative); scaled by 2^n.  The
+// head with 15 significant bits (22713 / 32768, so n * head is exact for
+// every |n| < 2^38; here |n| <= 1443) and a tail; e^r from its Taylor series
+// to degree 11 (truncation error below 1e-14 relative); scaled by 2^n.  The
 // argument is clamped at -1000, where e^x is 0 in fp64.  Relative error
-// below 1e-14 over [-708, 0] (checked against a correctly rounded exp).
-__device__ __forceinline__ double exp_nonpos(double x) {
+// below 1e-14 over [-708, 0]; a CPU test runs this same code on the host
+// against the C library's exp.
+__host__ __device__ inline double exp_nonpos(double x) {
   constexpr double kLog2E = 1.4426950408889634;
-  constexpr double kLn2Head = 0.693145751953125;        // 2839 / 4096
+  constexpr double kLn2Head = 0.693145751953125;        // 22713 / 32768
   constexpr double kLn2Tail = 1.4286068203094173e-06;   // ln 2 - head
   x = fmax(x, -1000.0);
   const double n = __builtin_rint(x * kLog2E);
