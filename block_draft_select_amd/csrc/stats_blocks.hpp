@@ -1,7 +1,7 @@
 // Device building blocks of S5 + S6 (verify against the target rows; P1
 // "DFlash 2: Block diffusion, wearing a drafter's coat", section "Lossless,
-// with conditions I did not used to state": accept with probability
-// min(1, p/q), resample from the residual on rejection; P2 "A 2B Drafter
+// with conditions I did not used to state": a draft survives with chance
+// min(1, p/q), a rejected one is replaced by a draw from the residual; P2 "A 2B Drafter
 // Made a 27B Model 3.4x Faster. Same Exact Output.", section "Caveats before
 // you rebuild your serving stack": greedy output equals the target's).
 //
@@ -9,7 +9,8 @@
 //   row held in registers (64 values per lane, 16-byte loads):
 //     greedy rows:   the chunk maximum and its first index;
 //     sampling rows: the chunk maximum m and S = sum over all tokens of
-//                    exp((z - m) / T), in fp32 with one v_exp_f32 per value.
+//                    exp((z - m) / T), in fp32 with one v_exp_f32 per value
+//                    (of the exactly formed difference z - m).
 //   The statistics do not depend on the candidates, so they stream in the
 //   same launch as the top-K; the candidates' own mass is taken out of their
 //   chunk in fp64 by the finalize.  The bf16 maximum first tries a packed
@@ -93,15 +94,18 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
         const uint32_t m16 = wave_max_u32(max(km & 0xFFFFu, km >> 16));
         m = __uint_as_float(bf16_of_k16(m16) << 16);
       }
+      // exponent (z - m) * log2(e) / T: the difference of two bf16 values
+      // is exact in fp32, so the terms near the maximum carry no error from
+      // m (m * k2 rounded once would shift every term of the chunk by a
+      // factor of relative size |m| / T * 2^-24, and overflow at tiny T)
       const float k2 = kLog2e / Tb;
-      const float mk = m * k2;
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
       for (int q = 0; q < 32; q += 2) {
-        s0 += __builtin_amdgcn_exp2f(fmaf(bf16_lo(x[q]), k2, -mk));
-        s1 += __builtin_amdgcn_exp2f(fmaf(bf16_hi(x[q]), k2, -mk));
-        s2 += __builtin_amdgcn_exp2f(fmaf(bf16_lo(x[q + 1]), k2, -mk));
-        s3 += __builtin_amdgcn_exp2f(fmaf(bf16_hi(x[q + 1]), k2, -mk));
+        s0 += __builtin_amdgcn_exp2f((bf16_lo(x[q]) - m) * k2);
+        s1 += __builtin_amdgcn_exp2f((bf16_hi(x[q]) - m) * k2);
+        s2 += __builtin_amdgcn_exp2f((bf16_lo(x[q + 1]) - m) * k2);
+        s3 += __builtin_amdgcn_exp2f((bf16_hi(x[q + 1]) - m) * k2);
       }
       st.m = m;
       st.s = wave_sum_f32((s0 + s1) + (s2 + s3));
@@ -138,14 +142,13 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
       for (int q = 1; q < 64; ++q) mx = max(mx, ord32(x[q]));
       const float m = __uint_as_float(unord32(wave_max_u32(mx)));
       const float k2 = kLog2e / Tb;
-      const float mk = m * k2;
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
       for (int q = 0; q < 64; q += 4) {
-        s0 += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(x[q + 0]), k2, -mk));
-        s1 += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(x[q + 1]), k2, -mk));
-        s2 += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(x[q + 2]), k2, -mk));
-        s3 += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(x[q + 3]), k2, -mk));
+        s0 += __builtin_amdgcn_exp2f((__uint_as_float(x[q + 0]) - m) * k2);
+        s1 += __builtin_amdgcn_exp2f((__uint_as_float(x[q + 1]) - m) * k2);
+        s2 += __builtin_amdgcn_exp2f((__uint_as_float(x[q + 2]) - m) * k2);
+        s3 += __builtin_amdgcn_exp2f((__uint_as_float(x[q + 3]) - m) * k2);
       }
       st.m = m;
       st.s = wave_sum_f32((s0 + s1) + (s2 + s3));
@@ -226,6 +229,9 @@ __device__ __forceinline__ void combine_row(FinLds& f, const ChunkStat* __restri
       const int fl = first_lane(c < n_chunk && m == M);
       if (fl < 64) first = base + fl;
     }
+    // no chunk maximum equals M only when every one is NaN (fmaxf skips
+    // them): the row then has no defined argmax, and chunk 0's stays in range
+    if (first == 0x7FFFFFFF) first = 0;
     if (lane == 0) {
       f.rowM[t] = M;
       f.rowArg[t] = st_row[first].arg;

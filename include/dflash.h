@@ -51,8 +51,12 @@
  *     their range are clamped into it, so no out-of-bounds access occurs;
  *     the outputs of such a stream are then unspecified.
  *   - Logits must be finite; NaN or infinite logits give unspecified
- *     results.  A temperature T[b] > 0 selects sampling for stream b; any
- *     other value (0, negative, NaN) selects greedy decoding.
+ *     results, but every token id the library writes still lies in [0, V)
+ *     (or is the -1 padding) and no access leaves its array.
+ *   - A finite temperature T[b] > 0 selects sampling for stream b; 0, a
+ *     negative value or NaN selects greedy decoding (the defined behaviour,
+ *     not an error: temperatures are device data, read only by the
+ *     kernels); +inf gives unspecified results.
  */
 #ifndef DFLASH_H
 #define DFLASH_H

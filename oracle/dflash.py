@@ -355,7 +355,7 @@ def cycle_stream(inp, b, chunk=CHUNK):
     return {
         "cand_idx": cand_idx, "cand_val": cand_val, "S": S,
         "path_rank": path, "draft_tok": draft, "q": q,
-        "accept_len": n, "out_tok": out,
+        "accept_len": n, "out_tok": out, "T": T,
         "margins": m_trace + m_verify,
     }
 

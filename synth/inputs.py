@@ -106,16 +106,20 @@ def _plant_row(rng, std, V, kind, recall, max_tries=200):
 
 def make(config_id, set_id=0, *, B=None, L=None, V=None, K=None, r=None,
          hidden=None, T=None, e_std=0.02, zero_E=False, ties=False,
-         plant="default", cycle=None):
+         plant="default", cycle=None, noise=None, boost=None, shift=None):
     """Build one input set.
 
     Keyword overrides shrink or vary a configuration for parity cases:
     ``e_std`` (0.3 gives the strong-selector variant whose paths leave the
     top-1), ``zero_E`` (all-zero embeddings), ``ties`` (logits quantised to
     multiples of 0.5 so that rows hold many exactly equal values), ``T``
-    (a scalar or a per-stream sequence) and ``plant`` (None disables
-    planted tokens).  Returns a dict of numpy arrays in storage form plus the
-    scalar dimensions.
+    (a scalar or a per-stream sequence), ``plant`` (None disables planted
+    tokens), ``noise`` (the target's noise level; 0 makes target rows
+    1..L copies of the drafter rows), ``boost`` (added to one uniformly
+    chosen token of every drafter row, and so of its target row, but not to
+    the extra target row L+1) and ``shift`` (a constant added to every drafter
+    and target logit, for large logits at low temperature).  Returns a dict
+    of numpy arrays in storage form plus the scalar dimensions.
     """
     cfg = dict(CONFIGS[config_id])
     for k, v in dict(B=B, L=L, V=V, K=K, r=r, hidden=hidden).items():
@@ -131,7 +135,8 @@ def make(config_id, set_id=0, *, B=None, L=None, V=None, K=None, r=None,
     Z = np.empty((Bn, Ln + 1, Vn), dtype=U.dtype)
     planted = np.full((Bn, Ln + 1), -1, dtype=np.int64)
     planted_rank = np.zeros((Bn, Ln + 1), dtype=np.int64)
-    std, noise = np.float32(cfg["u_std"]), np.float32(cfg["noise"])
+    std = np.float32(cfg["u_std"])
+    noise = np.float32(cfg["noise"] if noise is None else noise)
 
     def drafter_row(t):
         # t: 0-based row index; row Ln is the extra target row's source
@@ -149,6 +154,11 @@ def make(config_id, set_id=0, *, B=None, L=None, V=None, K=None, r=None,
     for b in range(Bn):
         for t in range(Ln + 1):
             row, y, rk = drafter_row(t)
+            if shift is not None:
+                row = _value(_store(row + np.float32(shift), lk), lk)
+            if boost is not None and t < Ln:
+                yb = int(rng.integers(0, Vn))
+                row[yb] = _value(_store(row[yb:yb + 1] + np.float32(boost), lk), lk)[0]
             if ties:
                 row = np.round(row * np.float32(2.0)) / np.float32(2.0)
             planted[b, t], planted_rank[b, t] = y, rk

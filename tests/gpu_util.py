@@ -52,9 +52,28 @@ def run_cycle(inp, dev=None, out=None, ws=None, device="cuda"):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
+def q_tolerance(ref):
+    """Per-entry bound on |q_gpu - q_ref| for one stream's sampled trace.
+
+    q_t = softmax(S[t, prev, :] / T) is formed in fp64 on both sides, but
+    from fp32 scores on the GPU: each score carries an absolute error of at
+    most about 2^-23 max(1, |S row|), which moves log q_t(j) by at most twice
+    that divided by T, so |dq| <= q * 2^-21 max(1, |S row|) / T with a
+    factor two to spare; 2e-6 covers the fp32 rounding of q itself."""
+    T, S, path = ref.get("T", 0.0), ref["S"], ref["path_rank"]
+    q = ref["q"]
+    tol = np.full(q.shape, 2e-6)
+    if T > 0:
+        prev = 0
+        for t in range(q.shape[0]):
+            tol[t] += q[t] * 2.0 ** -21 * max(1.0, float(np.abs(S[t, prev]).max())) / T
+            prev = int(path[t])
+    return tol
+
+
 def compare_stream(gpu, ref, b, check_q=True):
     """Assert the parity bar for stream b: exact integers, scores within
-    1e-4 relative (floor 1), q within 2e-6 absolute."""
+    1e-4 relative (floor 1), q within the bound of ``q_tolerance``."""
     L = ref["cand_idx"].shape[0]
     np.testing.assert_array_equal(gpu["cand_idx"][b], ref["cand_idx"], err_msg=f"cand_idx stream {b}")
     np.testing.assert_array_equal(gpu["cand_logit"][b].astype(np.float64), ref["cand_val"],
@@ -65,6 +84,6 @@ def compare_stream(gpu, ref, b, check_q=True):
     np.testing.assert_array_equal(gpu["path_rank"][b], ref["path_rank"], err_msg=f"path_rank stream {b}")
     np.testing.assert_array_equal(gpu["draft_tok"][b], ref["draft_tok"], err_msg=f"draft_tok stream {b}")
     if check_q:
-        assert np.all(np.abs(gpu["q"][b].astype(np.float64) - ref["q"]) <= 2e-6), f"q stream {b}"
+        assert np.all(np.abs(gpu["q"][b].astype(np.float64) - ref["q"]) <= q_tolerance(ref)), f"q stream {b}"
     assert int(gpu["accept_len"][b]) == int(ref["accept_len"]), f"accept_len stream {b}"
     np.testing.assert_array_equal(gpu["out_tok"][b], ref["out_tok"][: L + 1], err_msg=f"out_tok stream {b}")

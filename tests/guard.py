@@ -10,10 +10,16 @@ re-draws the stream's Philox seed (sampling decisions) or context vector h
 
 Thresholds (relative to the stated scale):
   trace_gap  1e-5 * max(1, |best score|)   fp32 score error is ~1e-7 relative
-  trace_cdf  1e-5 * total weight            fp32 scores enter exp()
-  accept     1e-5 * max(u q, p)             fp32 row sums (~1e-6 relative)
+  trace_cdf  1e-5 * total weight * sens_t   fp32 scores enter exp()
+  accept     1e-5 * max(u q, p) * sens_t    fp32 row sums (~1e-6 relative), q
   item_cdf   1e-5 (probability units)       fp32 chunk sums
   chunk_cdf  1e-9 * chunk mass              both sides fp64
+
+sens_t = max(1, 0.1 * max |S row| / T) at a sampled position t: the GPU's
+scores are fp32, so each carries an absolute error up to about 2^-23 |S|,
+which the trace's softmax turns into a relative error of about 2^-22 |S| / T
+in every weight of the row and in q_t; with large scores at a low
+temperature (|S| / T in the hundreds) that exceeds the plain 1e-5.
 """
 
 import numpy as np
@@ -23,8 +29,29 @@ from oracle import dflash
 THRESH = {"trace_gap": 1e-5, "trace_cdf": 1e-5, "accept": 1e-5, "item_cdf": 1e-5, "chunk_cdf": 1e-9}
 
 
-def violations(margins):
-    return [(k, v, s) for (k, v, s) in margins if v < THRESH[k] * s]
+def score_sensitivity(r):
+    """sens_t of every drafted position of one oracle result (1 when greedy)."""
+    T, S, path = r["T"], r["S"], r["path_rank"]
+    sens, prev = [], 0
+    for t in range(S.shape[0]):
+        sens.append(max(1.0, 0.1 * float(np.abs(S[t, prev]).max()) / T) if T > 0 else 1.0)
+        prev = int(path[t])
+    return sens
+
+
+def violations(margins, sens=None):
+    """Margins closer than their threshold.  The trace_cdf and accept
+    margins come in position order (one per drafted position reached), so
+    the i-th of each kind is scaled by sens[i]."""
+    bad, seen = [], {"trace_cdf": 0, "accept": 0}
+    for (k, v, s) in margins:
+        f = 1.0
+        if sens is not None and k in seen:
+            f = sens[min(seen[k], len(sens) - 1)]
+            seen[k] += 1
+        if v < THRESH[k] * s * f:
+            bad.append((k, v, s))
+    return bad
 
 
 def _redraw_h(inp, b, attempt):
@@ -50,7 +77,7 @@ def guarded(inp, streams=None, max_tries=40, guard_trace=True):
         b = int(b)
         for attempt in range(max_tries):
             r = dflash.cycle_stream(inp, b)
-            bad = violations(r["margins"])
+            bad = violations(r["margins"], score_sensitivity(r))
             if not guard_trace:
                 bad = [x for x in bad if x[0] != "trace_gap"]
             if not bad:

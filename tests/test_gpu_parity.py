@@ -48,6 +48,13 @@ SMALL = [
     ("bf16-L16", 4, dict(B=2, V=20000, hidden=256), True),
     ("bf16-r16-T06", 3, dict(B=3, V=8200, hidden=64, r=16, T=0.6), True),
     ("bf16-single-chunk", 3, dict(B=5, V=64, K=16, hidden=256, plant=None), True),
+    # large logits at a low temperature: the chunk sums must not lose the
+    # terms near each chunk's maximum to the rounding of m / T
+    ("bf16-T01-logits35", 3, dict(B=4, V=20008, hidden=256, T=0.1, shift=35.0), True),
+    ("bf16-T06-logits-40", 5, dict(B=6, V=12296, hidden=256, T=0.6, shift=-40.0), True),
+    # temperatures that are not positive (0, negative, -0, NaN) are greedy
+    ("bf16-nonpositive-T", 5, dict(B=6, V=12296, hidden=256,
+                                   T=[0.0, -1.0, float("nan"), 0.6, -0.0, 1.0]), True),
 ]
 
 
@@ -92,23 +99,37 @@ def test_zero_embeddings_independent_top1(ties):
         compare_stream(gpu, ref[b], b)
 
 
+# the five configurations at full size, every stream compared (the largest
+# in two halves, so that each test stays short; the halves share one input
+# set, whose redrawn seeds stay guard-clean for the streams already checked)
 FULL = [
     ("C1", 1, None),
     ("C2", 2, None),
-    ("C3", 3, [0, 13, 31]),
-    ("C4", 4, [0, 31]),
-    ("C5", 5, [0, 1, 2, 3, 127]),
+    ("C3", 3, None),
+    ("C4", 4, None),
+    ("C5-first-half", 5, range(0, 64)),
+    ("C5-second-half", 5, range(64, 128)),
 ]
+_FULL_INPUTS = {}
 
 
 @pytest.mark.parametrize("name,cid,streams", FULL, ids=[c[0] for c in FULL])
-def test_full_size_configs_sampled(name, cid, streams):
-    inp = synth.make(cid, set_id=0)
-    _say(f"[parity] full {name}: B={inp['B']} L={inp['L']} V={inp['V']} streams={streams}")
+def test_full_size_configs_every_stream(name, cid, streams):
+    if cid not in _FULL_INPUTS:
+        _FULL_INPUTS.clear()
+        _FULL_INPUTS[cid] = synth.make(cid, set_id=0)
+    inp = _FULL_INPUTS[cid]
+    streams = list(range(inp["B"]) if streams is None else streams)
+    _say(f"[parity] full {name}: B={inp['B']} L={inp['L']} V={inp['V']} streams {streams[0]}..{streams[-1]}")
     ref, redraws = guarded(inp, streams=streams)
     gpu = run_cycle(inp)
     for b in ref:
         compare_stream(gpu, ref[b], b)
+    L = int(inp["L"])
+    full = sum(int(r["accept_len"] == L) for r in ref.values())
+    acc = sum(int(r["accept_len"]) for r in ref.values())
+    _say(f"[parity] full {name}: {len(ref)} streams equal the oracle; {redraws} guard redraws; "
+         f"accepted drafts {acc}; streams accepting all {L}: {full}")
 
 
 # block sizes the serving runtimes use (blocks of 4 to 16 drafted
@@ -149,6 +170,24 @@ def test_extreme_shapes(name, cid, kw, streams):
     gpu = run_cycle(inp)
     for b in ref:
         compare_stream(gpu, ref[b], b)
+
+
+def test_all_nan_target_row_stays_in_range():
+    # a greedy target row whose every logit is NaN has no argmax (the
+    # results are unspecified) but the call must succeed and every emitted
+    # token stay in range; the other stream is unaffected
+    inp = synth.make(2, set_id=8, B=2, V=12296, hidden=256, T=0.0)
+    _say("[parity] all-NaN target row")
+    ref, _ = guarded(inp, streams=[0], guard_trace=False)
+    inp["Z"][1, 0] = 0x7FC0
+    inp["Z"][1, 2] = 0x7FC0
+    gpu = run_cycle(inp)
+    compare_stream(gpu, ref[0], 0)
+    V, L = inp["V"], inp["L"]
+    assert 0 <= gpu["accept_len"][1] <= L
+    n = int(gpu["accept_len"][1])
+    assert np.all((gpu["out_tok"][1][: n + 1] >= 0) & (gpu["out_tok"][1][: n + 1] < V))
+    assert np.all(gpu["out_tok"][1][n + 1:] == -1)
 
 
 def test_rows_without_admissible_values_stay_in_range():
