@@ -4,11 +4,11 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Shares no code with
 the HIP library and imports nothing from it.
 
 Source: P1 "DFlash 2: Block diffusion, wearing a drafter's coat", section "The
-architecture", sub-section "Suffix-decay convolution" (a two-tap dynamic
-depthwise convolution that repairs the accuracy fall-off toward the end of
-the block); P2 "A 2B Drafter Made a 27B Model 3.4x Faster. Same Exact
-Output.", section "The two fixes" (it mixes each position's representation
-with its immediate predecessor's).
+architecture", sub-section "Suffix-decay convolution" (a short convolution
+whose taps depend on the input, added so that the last positions of a block
+are drafted as well as the first ones); P2 "A 2B Drafter Made a 27B Model
+3.4x Faster. Same Exact Output.", section "The two fixes" (each block
+position is combined with the one just before it).
 
 Reading of what the pages leave open (the tap generator is not given):
   * depthwise, two taps: channel c of position t mixes only channel c of
