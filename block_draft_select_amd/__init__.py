@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 F32 = 0
 BF16 = 1
 K_MAX, L_MAX, R_MAX, V_MAX, CHUNK = 16, 16, 256, 2097152, 4096
+STATIC_SCRATCH_BYTES = 8 << 20
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
@@ -57,6 +58,7 @@ def _load():
         "dflash_verify": (I32, [D, P, P, P, P, P, P, U64, P, P, P, SZ, P]),
         "dflash_cycle": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dflash_cycle_maxsum": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dflash_cycle_static": (I32, [D, P, P, P, P, P, P, P, P, U64, P, P, P, P, P, P, P, P, P]),
         "dflash_conv2tap": (I32, [D, P, P, P, P, P]),
         "dflash_trace_viterbi": (I32, [D, P, P, P, P, P, P]),
         "dflash_topk_merge": (I32, [D, I32, ctypes.POINTER(I32), P, P, P, P, P]),
@@ -205,6 +207,27 @@ def dflash_cycle_maxsum(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_
                         stream=None):
     _cycle_call(lib.dflash_cycle_maxsum, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, ws,
                 cand_idx, cand_logit, S, path_rank, draft_tok, q, stream)
+
+
+def dflash_cycle_static(d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok,
+                        cand_idx=None, cand_logit=None, S=None, path_rank=None, draft_tok=None, q=None,
+                        stream=None):
+    """dflash_cycle on the library's own static scratch (no workspace argument)."""
+    R, lt, pt = d.B * d.L, _TORCH_LOGIT[d.logit_dtype], _TORCH_LOGIT[d.param_dtype]
+    _check(lib.dflash_cycle_static(
+        ctypes.byref(d), _ptr(U, "U", lt, R * d.V), _ptr(Z, "Z", lt, d.B * (d.L + 1) * d.V),
+        _ptr(x0, "x0", torch.int32, d.B), _ptr(E, "E", pt, d.V * d.r),
+        _ptr(W_g, "W_g", pt, d.hidden * d.r), _ptr(h, "h", pt, R * d.hidden),
+        _ptr(T, "T", torch.float32, d.B), _ptr(seed, "seed", torch.int64, d.B),
+        ctypes.c_uint64(int(cycle) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(accept_len, "accept_len", torch.int32, d.B),
+        _ptr(out_tok, "out_tok", torch.int32, d.B * (d.L + 1)),
+        _ptr(cand_idx, "cand_idx", torch.int32, R * d.K, optional=True),
+        _ptr(cand_logit, "cand_logit", torch.float32, R * d.K, optional=True),
+        _ptr(S, "S", torch.float32, R * d.K * d.K, optional=True),
+        _ptr(path_rank, "path_rank", torch.int32, R, optional=True),
+        _ptr(draft_tok, "draft_tok", torch.int32, R, optional=True),
+        _ptr(q, "q", torch.float32, R * d.K, optional=True), _stream(stream)))
 
 
 def dflash_topk_merge(d, shard_begin, cand_idx_parts, cand_logit_parts, cand_idx, cand_logit, stream=None):

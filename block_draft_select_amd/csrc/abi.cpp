@@ -408,6 +408,32 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z, c
                     cand_logit_opt, S_opt, path_rank_opt, draft_tok_opt, q_opt, ws, ws_bytes, stream);
 }
 
+dflash_status dflash_cycle_static(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0,
+                                  const void* E, const void* W_g, const void* h, const float* T,
+                                  const uint64_t* seed, uint64_t cycle, int32_t* accept_len, int32_t* out_tok,
+                                  int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
+                                  int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt, void* stream) {
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    const size_t need = dfk::ws_layout(*d).total;
+    if (need > DFLASH_STATIC_SCRATCH_BYTES)
+      return fail(DFLASH_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
+                                            " bytes of scratch, above the static maximum of " +
+                                            std::to_string((size_t)DFLASH_STATIC_SCRATCH_BYTES) +
+                                            " (use dflash_cycle with a workspace)");
+    if (dflash_status s = hip_status(dfk::static_scratch(&scratch, &scratch_bytes), "static scratch lookup"))
+      return s;
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+  // the library's own array stands in for the caller's workspace
+  return cycle_impl(false, d, U, Z, x0, E, W_g, h, T, seed, cycle, accept_len, out_tok, cand_idx_opt,
+                    cand_logit_opt, S_opt, path_rank_opt, draft_tok_opt, q_opt, scratch, scratch_bytes, stream);
+}
+
 dflash_status dflash_cycle_maxsum(const dflash_dims* d, const void* U, const void* Z, const int32_t* x0,
                                   const void* E, const void* W_g, const void* h, const float* T,
                                   const uint64_t* seed, uint64_t cycle, int32_t* accept_len, int32_t* out_tok,

@@ -110,6 +110,9 @@ hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const 
 hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, const void* Wt, float* y,
                            hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// device address and size of the library's static scratch on the current
+// device (looked up once per device)
+hipError_t static_scratch(void** out, size_t* bytes);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t st);
 

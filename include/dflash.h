@@ -75,6 +75,7 @@ extern "C" {
 #define DFLASH_R_MAX 256     /* embedding rank */
 #define DFLASH_V_MAX 2097152 /* vocabulary size */
 #define DFLASH_CHUNK 4096    /* tokens per first-level item of the residual draw */
+#define DFLASH_STATIC_SCRATCH_BYTES (8u << 20) /* the library's own scratch per GPU (dflash_cycle_static) */
 
 typedef int32_t dflash_status;
 enum {
@@ -213,6 +214,30 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
                            int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
                            int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* dflash_cycle without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The scratch is the library's
+ * own file-scope device array of DFLASH_STATIC_SCRATCH_BYTES (8 MiB) per
+ * GPU, held until the process ends; no call allocates or frees anything.
+ * Same arguments, results and launches as dflash_cycle otherwise.
+ *   - Sizes whose workspace (dflash_workspace_bytes) exceeds
+ *     DFLASH_STATIC_SCRATCH_BYTES are rejected with DFLASH_ERR_WORKSPACE
+ *     before anything is enqueued (the five benchmark shapes, up to
+ *     B = 128, L = 8, V = 262144, need at most 5.7 MiB).
+ *   - The first call on a device looks up the array's device address with
+ *     hipGetSymbolAddress (a host-side query, no allocation) while that
+ *     device is current; make that first call outside graph capture.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (the cycle needs none cleared): calls that overlap in
+ *     time on one GPU (concurrent streams, threads) race and must not. */
+dflash_status dflash_cycle_static(const dflash_dims* d, const void* U, const void* Z,
+                                  const int32_t* x0, const void* E, const void* W_g, const void* h,
+                                  const float* T, const uint64_t* seed, uint64_t cycle,
+                                  int32_t* accept_len, int32_t* out_tok,
+                                  int32_t* cand_idx_opt, float* cand_logit_opt, float* S_opt,
+                                  int32_t* path_rank_opt, int32_t* draft_tok_opt, float* q_opt,
+                                  void* stream);
 
 /* The whole cycle with the max-sum trace (dflash_trace_viterbi) in place of
  * the greedy/sampled walk, in three launches like dflash_cycle: its

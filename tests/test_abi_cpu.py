@@ -116,3 +116,17 @@ def test_null_and_misaligned_pointers_rejected(dfl):
     bad = dfl.dims(1, 17, 4096, 4, 16, 16, "bf16", "bf16")
     assert dfl.lib.dflash_trace_viterbi(ctypes.byref(bad), fake, fake, fake, fake, fake, None) == 1
     assert dfl.lib.dflash_profile_collect(42, None, None) == 1
+
+
+def test_static_cycle_rejects_sizes_beyond_its_scratch(dfl):
+    # B (L + 1) = 65535 rows of a tiny vocabulary need about 152 MiB of
+    # workspace, above the static scratch: rejected on the host, before any
+    # HIP call (this runs without a GPU)
+    d = dfl.dims(3855, 16, 64, 16, 16, 16, "bf16", "bf16")
+    assert dfl.workspace_bytes(d) > dfl.STATIC_SCRATCH_BYTES
+    nul = ctypes.c_void_p(0)
+    st = dfl.lib.dflash_cycle_static(ctypes.byref(d), *([nul] * 8), 0, *([nul] * 8), nul)
+    assert st == dfl.ERR_WORKSPACE
+    assert b"static maximum" in dfl.lib.dflash_last_error()
+    bad = dfl.dims(0, 8, 1024, 16, 256, 256, "f32", "f32")
+    assert dfl.lib.dflash_cycle_static(ctypes.byref(bad), *([nul] * 8), 0, *([nul] * 8), nul) == dfl.ERR_INVALID_ARG
