@@ -221,7 +221,31 @@ def softmax_T(z, T):
     return w / w.sum()
 
 
-def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
+def chunk_bounds(V, chunk=CHUNK, shard_begin=None):
+    """The first-level items of the residual draw: (lo, hi) token ranges.
+
+    Without a vocabulary split the tokens are cut into runs of ``chunk`` in
+    index order (the last one shorter).  With one (P1 "DFlash 2: Block
+    diffusion, wearing a drafter's coat", "The architecture", "Parallel
+    block drafting", and the serving runtimes of P2 "A 2B Drafter Made a
+    27B Model 3.4x Faster. Same Exact Output.", "Running it", where the
+    target's vocabulary may be split across devices) the cut restarts at
+    every shard boundary, so that no chunk straddles two shards: shard s
+    covers [shard_begin[s], shard_begin[s+1]) (the last up to V) and is cut
+    into runs of ``chunk`` from its own first token.  This build's reading:
+    the draw only needs the items to partition the tokens in index order,
+    so any such cut leaves the residual law unchanged.
+    """
+    starts = [0] if shard_begin is None else [int(s) for s in shard_begin]
+    ends = starts[1:] + [V]
+    out = []
+    for lo_s, hi_s in zip(starts, ends):
+        for lo in range(lo_s, hi_s, chunk):
+            out.append((lo, min(lo + chunk, hi_s)))
+    return out
+
+
+def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK, shard_begin=None):
     """Rejection-sampling verify of one stream's drafted path.
 
     ``Zrows`` [L+1, V] target logits (float64), ``cand_idx`` [L, K],
@@ -241,7 +265,8 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
            uses the fp64 uniforms u1 (words 0,1) and u2 (words 2,3) of the
            (seed; cycle, n+1, 1) block: u1 picks an item among
            [chunk 0..n_c-1 (non-candidate mass), candidate 0..K-1], u2 picks
-           a non-candidate token inside a picked chunk.
+           a non-candidate token inside a picked chunk.  The chunks are those
+           of :func:`chunk_bounds` (``shard_begin``: a vocabulary split).
 
     Returns (accept_len, out_tok int64[L+1] padded with -1, margins).
     """
@@ -287,8 +312,9 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
         cand_mass = np.zeros(0)
     r = p.copy()
     r[cand] = 0.0                            # non-candidate mass only
-    n_c = -(-V // chunk)
-    chunk_mass = np.array([r[c * chunk:(c + 1) * chunk].sum() for c in range(n_c)])
+    bounds = chunk_bounds(V, chunk, shard_begin)
+    n_c = len(bounds)
+    chunk_mass = np.array([r[lo:hi].sum() for lo, hi in bounds])
     items = np.concatenate([chunk_mass, cand_mass])
     if not items.sum() > 0:
         items = np.concatenate([chunk_mass, p[cand]])
@@ -303,12 +329,13 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
     if m >= n_c:
         tok = int(cand[m - n_c])
     else:
-        seg = r[m * chunk:(m + 1) * chunk]
+        lo, hi = bounds[m]
+        seg = r[lo:hi]
         cs = np.cumsum(seg)
         tgt = u2 * cs[-1]
         i = _first_above(cs, tgt)
         margins.append(("chunk_cdf", _cdf_margin(cs, i, tgt), cs[-1]))
-        tok = m * chunk + i
+        tok = lo + i
     out[:n] = draft[:n]
     out[n] = tok
     return n, out, margins
@@ -318,13 +345,16 @@ def verify_stream(Zrows, cand_idx, path_rank, q, T, seed, cycle, chunk=CHUNK):
 # one whole cycle of one stream, and of a batch
 # --------------------------------------------------------------------------
 
-def cycle_stream(inp, b, chunk=CHUNK):
+def cycle_stream(inp, b, chunk=CHUNK, shard_begin=None):
     """All steps S1..S6 for stream ``b`` of an input set.
 
     ``inp`` is a mapping with keys B, L, V, K, r, hidden, logit_kind,
     param_kind, U [B,L,V], Z [B,L+1,V], x0 [B], E [V,r], W [r,hidden],
     h [B,L,hidden], T [B], seed [B], cycle (int).  Arrays hold storage
     values (uint16 bf16 patterns or float32); everything is widened here.
+    ``shard_begin``: the first tokens of a vocabulary split, which moves the
+    residual draw's chunk boundaries (:func:`chunk_bounds`); the candidates,
+    scores and path do not depend on it.
     """
     L, K = int(inp["L"]), int(inp["K"])
     lk, pk = inp["logit_kind"], inp["param_kind"]
@@ -351,7 +381,7 @@ def cycle_stream(inp, b, chunk=CHUNK):
 
     path, draft, q, m_trace = trace_stream(S, cand_idx, T, seed, cyc)
     Zr = widen(inp["Z"][b], lk)                      # [L+1, V]
-    n, out, m_verify = verify_stream(Zr, cand_idx, path, q, T, seed, cyc, chunk=chunk)
+    n, out, m_verify = verify_stream(Zr, cand_idx, path, q, T, seed, cyc, chunk=chunk, shard_begin=shard_begin)
     return {
         "cand_idx": cand_idx, "cand_val": cand_val, "S": S,
         "path_rank": path, "draft_tok": draft, "q": q,
@@ -360,8 +390,8 @@ def cycle_stream(inp, b, chunk=CHUNK):
     }
 
 
-def cycle(inp, streams=None, chunk=CHUNK):
+def cycle(inp, streams=None, chunk=CHUNK, shard_begin=None):
     """:func:`cycle_stream` for every stream in ``streams`` (default: all)."""
     if streams is None:
         streams = range(int(inp["B"]))
-    return {int(b): cycle_stream(inp, int(b), chunk=chunk) for b in streams}
+    return {int(b): cycle_stream(inp, int(b), chunk=chunk, shard_begin=shard_begin) for b in streams}

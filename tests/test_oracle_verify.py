@@ -232,3 +232,86 @@ def test_non_positive_or_nan_temperature_is_greedy(T):
         Z = dflash.widen(b["Z"][s], "bf16")
         n_ref, out_ref = _greedy_decode(Z, rb["draft_tok"])
         assert rb["accept_len"] == n_ref and list(rb["out_tok"][: n_ref + 1]) == out_ref
+
+
+# ---------------------------------------------------------------- vocabulary split
+
+def test_chunk_bounds_partition_the_vocabulary():
+    # the items always cover every token once, in index order, and never
+    # straddle a shard boundary
+    for V, chunk, begins in ((151936, 4096, None), (151936, 4096, [0, 18992, 37984, 56976, 75968, 94960,
+                                                                    113952, 132944]),
+                             (100, 7, [0, 13, 14, 60]), (64, 8, [0])):
+        b = dflash.chunk_bounds(V, chunk, begins)
+        assert b[0][0] == 0 and b[-1][1] == V
+        assert all(b[i][1] == b[i + 1][0] for i in range(len(b) - 1))
+        assert all(0 < hi - lo <= chunk for lo, hi in b)
+        for s in (begins or [0]):
+            assert any(lo == s for lo, _ in b)
+
+
+def test_aligned_or_single_shard_split_changes_nothing():
+    # shard boundaries on the chunk grid (262144 / 8) or a single shard give
+    # the unsplit chunks, so every output is identical
+    inp = synth.make(5, set_id=31, B=3, V=32768, hidden=64)
+    for begins in ([0], [0, 4096, 8192, 12288, 16384, 20480, 24576, 28672]):
+        for s in range(inp["B"]):
+            a, b = dflash.cycle_stream(inp, s), dflash.cycle_stream(inp, s, shard_begin=begins)
+            assert a["accept_len"] == b["accept_len"]
+            np.testing.assert_array_equal(a["out_tok"], b["out_tok"])
+
+
+def test_ragged_split_moves_only_the_in_chunk_draw():
+    # with shard boundaries off the grid the chunks differ, so the token a
+    # given uniform lands on may differ, but only through the residual draw:
+    # the candidates, path, q and accept count never change
+    inp = synth.make(3, set_id=32, B=4, V=20008, hidden=64)
+    begins = [0, 2501, 5002, 7503, 10004, 12505, 15006, 17507]
+    for s in range(inp["B"]):
+        a, b = dflash.cycle_stream(inp, s), dflash.cycle_stream(inp, s, shard_begin=begins)
+        for k in ("cand_idx", "path_rank", "draft_tok", "q"):
+            np.testing.assert_array_equal(a[k], b[k])
+        assert a["accept_len"] == b["accept_len"]
+        np.testing.assert_array_equal(a["out_tok"][: a["accept_len"]], b["out_tok"][: b["accept_len"]])
+
+
+@pytest.mark.parametrize("begins", [[0, 7], [0, 3, 11, 17], [0, 1, 2, 19]])
+def test_residual_law_is_unchanged_by_a_vocabulary_split(begins):
+    # the residual draw over a chunk grid that restarts at each shard
+    # boundary still follows the normalised residual (forced rejection at
+    # position 1, as in the chunk-size test)
+    rng = np.random.default_rng(18)
+    V, K, T = 20, 4, 1.0
+    Z = rng.standard_normal((2, V))
+    cand = rng.permutation(V)[:K][None, :]
+    p = special.softmax(Z[0] / T)
+    q = np.zeros((1, K))
+    q[0] = [0.7, 0.1, 0.1, 0.1]
+    resid = p.copy()
+    resid[cand[0]] = np.maximum(0.0, p[cand[0]] - q[0])
+    resid /= resid.sum()
+    d_rank = np.array([int(np.argmax(q[0] - p[cand[0]]))])
+    toks = []
+    for c in range(4000):
+        n, out, _ = dflash.verify_stream(Z, cand, d_rank, q, T, 37, c, chunk=4, shard_begin=begins)
+        if n == 0:
+            toks.append(int(out[0]))
+    assert len(toks) > 1000
+    assert _chi2_pvalue(np.array(toks), resid) > 1e-4
+
+
+def test_bonus_law_is_unchanged_by_a_vocabulary_split():
+    # the bonus row has no candidates: the two-level draw over the split
+    # chunk grid must follow p of the last row
+    rng = np.random.default_rng(6)
+    V, L, T = 24, 1, 0.8
+    Z = rng.standard_normal((L + 1, V))
+    cand = np.stack([rng.permutation(V) for _ in range(L)])
+    S = np.stack([np.tile(Z[t, cand[t]], (V, 1)) for t in range(L)])
+    bonus = []
+    for c in range(3000):
+        path, draft, q, _ = dflash.trace_stream(S, cand, T, 3, c)
+        n, out, _ = dflash.verify_stream(Z, cand, path, q, T, 3, c, chunk=5, shard_begin=[0, 9, 10, 17])
+        assert n == L
+        bonus.append(int(out[L]))
+    assert _chi2_pvalue(np.array(bonus), special.softmax(Z[L] / T)) > 1e-4
