@@ -23,7 +23,7 @@ STATIC_SCRATCH_BYTES = 8 << 20
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 KERNELS = ("topk", "gate", "scores", "trace", "stats", "finalize", "cycle_stream", "cycle_scores",
-           "cycle_finalize", "conv2tap", "trace_viterbi", "topk_merge")
+           "cycle_finalize", "conv2tap", "trace_viterbi", "topk_merge", "shard_stats", "shard_finalize")
 
 
 class dflash_dims(ctypes.Structure):
@@ -62,6 +62,10 @@ def _load():
         "dflash_conv2tap": (I32, [D, P, P, P, P, P]),
         "dflash_trace_viterbi": (I32, [D, P, P, P, P, P, P]),
         "dflash_topk_merge": (I32, [D, I32, ctypes.POINTER(I32), P, P, P, P, P]),
+        "dflash_shard_stats_bytes": (I32, [D, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
+        "dflash_shard_stats": (I32, [D, I32, ctypes.POINTER(I32), I32, P, P, P, P]),
+        "dflash_verify_shards": (I32, [D, I32, ctypes.POINTER(I32), ctypes.POINTER(P), P, P, P, P, P, P, U64, P, P,
+                                       P]),
         "dflash_read_probe": (I32, [P, SZ, P, P]),
         "dflash_copy_probe": (I32, [P, P, SZ, P]),
         "dflash_kernel_name": (ctypes.c_char_p, [I32]),
@@ -239,6 +243,46 @@ def dflash_topk_merge(d, shard_begin, cand_idx_parts, cand_logit_parts, cand_idx
                                  _ptr(cand_logit_parts, "cand_logit_parts", torch.float32, n * R * d.K),
                                  _ptr(cand_idx, "cand_idx", torch.int32, R * d.K),
                                  _ptr(cand_logit, "cand_logit", torch.float32, R * d.K), _stream(stream)))
+
+
+def _begins(shard_begin):
+    n = len(shard_begin)
+    return n, (ctypes.c_int32 * n)(*[int(v) for v in shard_begin])
+
+
+def shard_stats_bytes(d, shard_begin):
+    n, begins = _begins(shard_begin)
+    out = ctypes.c_size_t(0)
+    _check(lib.dflash_shard_stats_bytes(ctypes.byref(d), n, begins, ctypes.byref(out)))
+    return out.value
+
+
+def dflash_shard_stats(d, shard_begin, shard, Z_shard, T, stats, stream=None):
+    """Statistics of shard ``shard`` (its rows ``Z_shard`` [B, L+1, width])
+    into its columns of ``stats`` (a uint8 tensor of shard_stats_bytes)."""
+    n, begins = _begins(shard_begin)
+    hi = shard_begin[shard + 1] if shard + 1 < n else d.V
+    width = int(hi) - int(shard_begin[shard])
+    _check(lib.dflash_shard_stats(ctypes.byref(d), n, begins, int(shard),
+                                  _ptr(Z_shard, "Z_shard", _TORCH_LOGIT[d.logit_dtype], d.B * (d.L + 1) * width),
+                                  _ptr(T, "T", torch.float32, d.B), _ptr(stats, "stats", torch.uint8),
+                                  _stream(stream)))
+
+
+def dflash_verify_shards(d, shard_begin, Z_shards, stats, cand_idx, path_rank, q, T, seed, cycle, accept_len,
+                         out_tok, stream=None):
+    """``Z_shards``: one [B, L+1, width] tensor per shard."""
+    n, begins = _begins(shard_begin)
+    R = d.B * d.L
+    zp = (ctypes.c_void_p * n)(*[_ptr(z, "Z_shards[]", _TORCH_LOGIT[d.logit_dtype]).value for z in Z_shards])
+    _check(lib.dflash_verify_shards(ctypes.byref(d), n, begins, zp, _ptr(stats, "stats", torch.uint8),
+                                    _ptr(cand_idx, "cand_idx", torch.int32, R * d.K),
+                                    _ptr(path_rank, "path_rank", torch.int32, R),
+                                    _ptr(q, "q", torch.float32, R * d.K),
+                                    _ptr(T, "T", torch.float32, d.B), _ptr(seed, "seed", torch.int64, d.B),
+                                    ctypes.c_uint64(int(cycle) & 0xFFFFFFFFFFFFFFFF),
+                                    _ptr(accept_len, "accept_len", torch.int32, d.B),
+                                    _ptr(out_tok, "out_tok", torch.int32, d.B * (d.L + 1)), _stream(stream)))
 
 
 def dflash_trace_viterbi(d, S, cand_idx, path_rank, draft_tok, q, stream=None):

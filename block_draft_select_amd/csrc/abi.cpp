@@ -320,6 +320,91 @@ dflash_status dflash_topk_merge(const dflash_dims* d, int32_t n_shards, const in
   }
 }
 
+// the vocabulary split of the verify: shard boundaries, chunk bases and
+// (when Z_shards is given) each shard's rows
+static dflash_status make_shard_map(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                    const void* const* Z_shards, dfk::ShardMap& m) {
+  if (n_shards < 1 || n_shards > DFLASH_MAX_SHARDS)
+    return fail(DFLASH_ERR_INVALID_ARG, "n_shards must be in 1 .. DFLASH_MAX_SHARDS");
+  if (!shard_begin) return fail(DFLASH_ERR_INVALID_ARG, "shard_begin is NULL");
+  const int unit = d->logit_dtype == DFLASH_BF16 ? 8 : 4;
+  m.n = n_shards;
+  m.cbase[0] = 0;
+  for (int s = 0; s < n_shards; ++s) {
+    const int64_t lo = shard_begin[s], hi = s + 1 < n_shards ? shard_begin[s + 1] : d->V;
+    if ((s == 0 && lo != 0) || hi <= lo || hi > d->V || lo % unit)
+      return fail(DFLASH_ERR_INVALID_ARG, "shards must start at 0, increase, end by V, and begin at multiples of "
+                                          "8 tokens (bf16) or 4 (fp32)");
+    m.begin[s] = (int32_t)lo;
+    m.cbase[s + 1] = m.cbase[s] + (int32_t)((hi - lo + dfk::kChunk - 1) / dfk::kChunk);
+    m.Z[s] = nullptr;
+    if (Z_shards) {
+      if (!Z_shards[s]) return fail(DFLASH_ERR_INVALID_ARG, "a shard's Z is NULL");
+      if (!aligned16(Z_shards[s])) return fail(DFLASH_ERR_INVALID_ARG, "a shard's Z is not 16-byte aligned");
+      m.Z[s] = Z_shards[s];
+    }
+  }
+  m.begin[n_shards] = d->V;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_shard_stats_bytes(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                       size_t* bytes) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (!bytes) return fail(DFLASH_ERR_INVALID_ARG, "bytes is NULL");
+    dfk::ShardMap m{};
+    if (dflash_status s = make_shard_map(d, n_shards, shard_begin, nullptr, m)) return s;
+    *bytes = (size_t)d->B * (d->L + 1) * m.cbase[m.n] * sizeof(dfk::ChunkStat);
+    return DFLASH_OK;
+  } catch (...) {
+    return fail(DFLASH_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+dflash_status dflash_shard_stats(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin, int32_t shard,
+                                 const void* Z_shard, const float* T, void* stats, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    dfk::ShardMap m{};
+    if (dflash_status s = make_shard_map(d, n_shards, shard_begin, nullptr, m)) return s;
+    if (shard < 0 || shard >= n_shards) return fail(DFLASH_ERR_INVALID_ARG, "shard must be in 0 .. n_shards - 1");
+    if (dflash_status s = check_ptrs({{Z_shard, "Z_shard", true}, {T, "T", false}, {stats, "stats", true}})) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_SHARD_STATS, st, [&] {
+      return dfk::launch_shard_stats(*d, m, shard, Z_shard, T, static_cast<dfk::ChunkStat*>(stats), st);
+    }), "shard stats launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
+dflash_status dflash_verify_shards(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                   const void* const* Z_shards, const void* stats, const int32_t* cand_idx,
+                                   const int32_t* path_rank, const float* q, const float* T, const uint64_t* seed,
+                                   uint64_t cycle, int32_t* accept_len, int32_t* out_tok, void* stream) {
+  try {
+    g_err.clear();
+    if (dflash_status s = check_dims(d)) return s;
+    if (!Z_shards) return fail(DFLASH_ERR_INVALID_ARG, "Z_shards is NULL");
+    dfk::ShardMap m{};
+    if (dflash_status s = make_shard_map(d, n_shards, shard_begin, Z_shards, m)) return s;
+    if (dflash_status s = check_ptrs({{stats, "stats", true}, {cand_idx, "cand_idx", false},
+                                      {path_rank, "path_rank", false}, {q, "q", false}, {T, "T", false},
+                                      {seed, "seed", false}, {accept_len, "accept_len", false},
+                                      {out_tok, "out_tok", false}})) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_status(timed(DFLASH_KERNEL_SHARD_FINALIZE, st, [&] {
+      return dfk::launch_finalize_shards(*d, m, cand_idx, path_rank, q, T, seed, cycle,
+                                         static_cast<const dfk::ChunkStat*>(stats), accept_len, out_tok, st);
+    }), "shard finalize launch");
+  } catch (...) {
+    return fail(DFLASH_ERR_HIP, "internal error");
+  }
+}
+
 dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
                                    int32_t* draft_tok, float* q, void* stream) {
   try {
@@ -483,7 +568,8 @@ dflash_status dflash_copy_probe(void* dst, const void* src, size_t bytes, void* 
 const char* dflash_kernel_name(int32_t kernel) {
   static const char* names[DFLASH_KERNEL_COUNT] = {"topk", "gate", "scores", "trace", "stats", "finalize",
                                                    "cycle_stream", "cycle_scores", "cycle_finalize", "conv2tap",
-                                                   "trace_viterbi", "topk_merge"};
+                                                   "trace_viterbi", "topk_merge", "shard_stats",
+                                                   "shard_finalize"};
   return (kernel >= 0 && kernel < DFLASH_KERNEL_COUNT) ? names[kernel] : "";
 }
 

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kFinThreads) void trace_finalize_kernel(
     int32_t* __restrict__ draft_tok, float* __restrict__ q, const ChunkStat* __restrict__ stats,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
   __shared__ FinLds f;
-  finalize_stream<DT, MODE>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, jstar, qtab,
+  finalize_stream<DT, MODE>(f, blockIdx.x, OneVocab{Z, V}, L, V, K, n_chunk, T, seed, cycle, cand_idx, zc, jstar, qtab,
                             path_rank, draft_tok, q, stats, accept_len, out_tok);
 }
 

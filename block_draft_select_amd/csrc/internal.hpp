@@ -81,8 +81,24 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
 struct ShardBegins {
   int32_t begin[DFLASH_MAX_SHARDS];
 };
+// a vocabulary split for the verify: shard s covers tokens
+// [begin[s], begin[s + 1]) (begin[n] = V), its residual-draw chunks are
+// cbase[s] .. cbase[s + 1] - 1 (the grid restarts at each shard), and its
+// target rows Z[s] are [B, L + 1, begin[s + 1] - begin[s]]
+struct ShardMap {
+  int32_t n;
+  int32_t begin[DFLASH_MAX_SHARDS + 1];
+  int32_t cbase[DFLASH_MAX_SHARDS + 1];
+  const void* Z[DFLASH_MAX_SHARDS];
+};
 hipError_t launch_topk_merge(const dflash_dims& d, int n_shards, const ShardBegins& sb, const int32_t* idx_parts,
                              const float* val_parts, int32_t* cand_idx, float* cand_logit, hipStream_t st);
+hipError_t launch_shard_stats(const dflash_dims& d, const ShardMap& m, int shard, const void* Zs, const float* T,
+                              ChunkStat* stats, hipStream_t st);
+hipError_t launch_finalize_shards(const dflash_dims& d, const ShardMap& m, const int32_t* cand_idx,
+                                  const int32_t* path_rank, const float* q, const float* T, const uint64_t* seed,
+                                  uint64_t cycle, const ChunkStat* stats, int32_t* accept_len, int32_t* out_tok,
+                                  hipStream_t st);
 hipError_t launch_trace_viterbi(const dflash_dims& d, const float* S, const int32_t* cand_idx, int32_t* path_rank,
                                 int32_t* draft_tok, float* q, hipStream_t st);
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,

@@ -165,12 +165,13 @@ __device__ __forceinline__ double logit_at(const void* Z, size_t i) {
 }
 
 // the TPT logits of tokens e0 .. e0 + TPT - 1 of the row starting at element
-// zr, widened to fp64.  Units of TPT tokens lie wholly inside or outside the
-// row (V is a multiple of 8 for bf16 and of 4 for fp32); units past V read
-// as -inf.
+// zr, widened to fp64 (e0 counted from the row's first token).  Units of TPT
+// tokens lie wholly inside or outside [0, hi) (row widths and chunk ends are
+// multiples of 8 for bf16 and of 4 for fp32); units past hi read as -inf.
 template <int DT, int TPT>
-__device__ __forceinline__ void load_tokens(const void* __restrict__ Z, size_t zr, int e0, int V, double (&zv)[TPT]) {
+__device__ __forceinline__ void load_tokens(const void* __restrict__ Z, size_t zr, int e0, int hi, double (&zv)[TPT]) {
   static_assert(TPT == 4, "4 tokens per thread");
+  const int V = hi;
   if (DT == DFLASH_BF16) {
     uint2 v = make_uint2(0xFF80FF80u, 0xFF80FF80u);
     if (e0 < V) v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Z) + zr + e0);
@@ -187,6 +188,63 @@ __device__ __forceinline__ void load_tokens(const void* __restrict__ Z, size_t z
     zv[3] = (double)__uint_as_float(v.w);
   }
 }
+
+// Where the residual draw's first-level chunks lie and where a token's
+// target logit is stored.  OneVocab: one contiguous vocabulary [0, V), rows
+// of V logits, chunks of kChunk tokens from token 0.  SplitVocab: a
+// vocabulary split into shards, each with its own [B, L + 1, width] rows;
+// the chunk grid restarts at every shard's first token.  Both give, for a
+// chunk id, its token range [lo, hi) and where its logits live.
+struct ChunkLoc {
+  int lo, hi;        // global token range of the chunk
+  const void* Zs;    // the rows holding it (the whole vocabulary or a shard)
+  int base, width;   // first global token and width of those rows
+};
+
+struct OneVocab {
+  const void* Z;
+  int V;
+  __device__ __forceinline__ int chunk_of(int tok) const { return tok / kChunk; }
+  __device__ __forceinline__ ChunkLoc chunk(int c) const {
+    const int lo = c * kChunk;
+    return ChunkLoc{lo, min(lo + kChunk, V), Z, 0, V};
+  }
+  template <int DT>
+  __device__ __forceinline__ double logit(size_t row, int tok) const {
+    return logit_at<DT>(Z, row * (size_t)V + tok);
+  }
+};
+
+struct SplitVocab {
+  const ShardMap& m;
+  __device__ __forceinline__ int shard_of(int tok) const {
+    int lo = 0, hi = m.n - 1;  // the last shard whose first token is <= tok
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (m.begin[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  __device__ __forceinline__ int chunk_of(int tok) const {
+    const int s = shard_of(tok);
+    return m.cbase[s] + (tok - m.begin[s]) / kChunk;
+  }
+  __device__ __forceinline__ ChunkLoc chunk(int c) const {
+    int lo = 0, hi = m.n - 1;  // the last shard whose first chunk is <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (m.cbase[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo, b0 = m.begin[s], b1 = m.begin[s + 1];
+    const int t0 = b0 + (c - m.cbase[s]) * kChunk;
+    return ChunkLoc{t0, min(t0 + kChunk, b1), m.Z[s], b0, b1 - b0};
+  }
+  template <int DT>
+  __device__ __forceinline__ double logit(size_t row, int tok) const {
+    const int s = shard_of(tok), b0 = m.begin[s];
+    return logit_at<DT>(m.Z[s], row * (size_t)(m.begin[s + 1] - b0) + (tok - b0));
+  }
+};
 
 constexpr int kFinThreads = 1024;  // 16 waves: the parallel phases split 16 ways
 constexpr int kFinWaves = kFinThreads / kWave;
@@ -205,6 +263,7 @@ struct FinLds {
   double zc[DFLASH_L_MAX][DFLASH_K_MAX];            // candidate target logits
   float qs[DFLASH_L_MAX][DFLASH_K_MAX];
   int cand[DFLASH_L_MAX][DFLASH_K_MAX];
+  int cchunk[DFLASH_L_MAX][DFLASH_K_MAX];           // the residual-draw chunk of each candidate
   int rank[DFLASH_L_MAX];
   uint4 rnd0[DFLASH_L_MAX];                         // (cycle, t + 1, 0) blocks
   uint4 rnd1[DFLASH_L_MAX + 1];                     // (cycle, t + 1, 1) blocks
@@ -267,7 +326,7 @@ __device__ __forceinline__ int pick_item(const FinLds& f, const ChunkStat* __res
   // the chunk of each of the row's candidates, in registers
   int cchunk[DFLASH_K_MAX];
 #pragma unroll
-  for (int k = 0; k < DFLASH_K_MAX; ++k) cchunk[k] = k < nk ? f.cand[t][k] / kChunk : -1;
+  for (int k = 0; k < DFLASH_K_MAX; ++k) cchunk[k] = k < nk ? f.cchunk[t][k] : -1;
   const int n_item = n_chunk + nk;
   auto item = [&](int i, bool resid) -> double {
     if (i < n_chunk) {
@@ -345,8 +404,8 @@ __device__ __forceinline__ const float* q_row_of(const FinLds& f, int t, int K) 
 // one-hot q.  kFinVerify: path_rank and q are inputs.  In the first two
 // modes zc_pre holds the candidates' target logits [B, L, K] (fp32-exact
 // values); otherwise it is not read and they are gathered here.
-template <int DT, int MODE>
-__device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, int L, int V, int K, int n_chunk,
+template <int DT, int MODE, class G>
+__device__ void finalize_stream(FinLds& f, int b, const G& geo, int L, int V, int K, int n_chunk,
                                 const float* __restrict__ T, const uint64_t* __restrict__ seed, uint64_t cycle,
                                 const int32_t* __restrict__ cand_idx, const float* __restrict__ zc_pre,
                                 const int32_t* __restrict__ jstar, const float* __restrict__ qtab,
@@ -359,7 +418,6 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   const bool greedy = !(Tb > 0.0f);
   const double invT = greedy ? 0.0 : 1.0 / (double)Tb;  // every exp((x - y) / T) is taken as exp_nonpos((x - y) * invT)
   const uint64_t sd = seed[b];
-  const size_t Vs = (size_t)V;
   const size_t zrow0 = (size_t)b * (L + 1);
   const ChunkStat* st_all = stats + zrow0 * n_chunk;
   const int n_terms = (L + 1) * n_chunk;
@@ -404,8 +462,9 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     const int t = tid / K, k = tid - (tid / K) * K;
     const int ci = clamp_idx(ci_raw, V);
     f.cand[t][k] = ci;
+    f.cchunk[t][k] = geo.chunk_of(ci);
     if (MODE == kFinVerify) f.qs[t][k] = q_raw;
-    if (!greedy) f.zc[t][k] = MODE != kFinVerify ? (double)zc_raw : logit_at<DT>(Z, (zrow0 + t) * Vs + ci);
+    if (!greedy) f.zc[t][k] = MODE != kFinVerify ? (double)zc_raw : geo.template logit<DT>(zrow0 + t, ci);
   }
   if (MODE == kFinVerify && tid < L) f.rank[tid] = clamp_idx(pr_raw, K);
   if (MODE != kFinVerify) {
@@ -550,11 +609,12 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
   } else {
     // (4) draw inside chunk `pick`: kFinTpt consecutive tokens per thread;
     // every weight is computed and masked afterwards (no branch per token)
-    const int c0 = pick * kChunk;
+    const ChunkLoc cl = geo.chunk(pick);
+    const int c0 = cl.lo;
     const int e0 = c0 + tid * kFinTpt;
     const double mc = (double)(cached ? f.ms[ts * n_chunk + pick].x : st[pick].m);
     double zv[kFinTpt];
-    load_tokens<DT, kFinTpt>(Z, (zrow0 + ts) * Vs, e0, V, zv);
+    load_tokens<DT, kFinTpt>(cl.Zs, (zrow0 + ts) * (size_t)cl.width, e0 - cl.base, cl.hi - cl.base, zv);
     // bit i set when token e0 + i is a candidate of row ts
     uint32_t cmask = 0;
 #pragma unroll
@@ -568,7 +628,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
 #pragma unroll
     for (int i = 0; i < kFinTpt; ++i) {
       const double ex = exp_nonpos((zv[i] - mc) * invT);
-      const double w = (e0 + i < V && !((cmask >> i) & 1u)) ? ex : 0.0;
+      const double w = (e0 + i < cl.hi && !((cmask >> i) & 1u)) ? ex : 0.0;
       if (w > 0.0) last_pos = e0 + i;
       run += w;
       wv[i] = run;
@@ -613,7 +673,7 @@ __device__ void finalize_stream(FinLds& f, int b, const void* __restrict__ Z, in
     else if (pos)
       tok = __builtin_amdgcn_readlane(last_pos, 63 - __builtin_clzll(pos));
     else
-      tok = min(V - 1, c0);
+      tok = c0;
     if (lane <= L) out_tok[o + lane] = lane < ts ? f.cand[lane][f.rank[lane]] : (lane == ts ? tok : -1);
     if (lane == 0) accept_len[b] = ts;
     return;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ path_rank, const float* __restrict__ q, const ChunkStat* __restrict__ stats,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok) {
   __shared__ FinLds f;
-  finalize_stream<DT, kFinVerify>(f, blockIdx.x, Z, L, V, K, n_chunk, T, seed, cycle, cand_idx, nullptr, nullptr,
+  finalize_stream<DT, kFinVerify>(f, blockIdx.x, OneVocab{Z, V}, L, V, K, n_chunk, T, seed, cycle, cand_idx, nullptr, nullptr,
                              nullptr, const_cast<int32_t*>(path_rank), nullptr, const_cast<float*>(q), stats,
                              accept_len, out_tok);
 }

@@ -146,6 +146,51 @@ dflash_status dflash_topk_merge(const dflash_dims* d, int32_t n_shards, const in
                                 const int32_t* cand_idx_parts, const float* cand_logit_parts,
                                 int32_t* cand_idx, float* cand_logit, void* stream);
 
+/* S5 over a vocabulary split -- the chunk statistics of one shard's target
+ * rows (P1 "Lossless, with conditions I did not used to state"; the split
+ * follows a tensor-parallel LM head, P2 "Running it").  Shard s covers
+ * tokens [shard_begin[s], shard_begin[s+1]) (the last one up to V) and holds
+ * its own rows Z_shard [B, L + 1, width].  The residual draw's chunks
+ * restart at every shard's first token (DFLASH_CHUNK tokens each, the last
+ * one of a shard shorter), so each shard's statistics depend only on its
+ * own logits.  This call writes shard `shard`'s columns of `stats`, the
+ * statistics of the whole vocabulary: [B, L + 1, C] records of 16 bytes,
+ * C = sum over shards of ceil(width / DFLASH_CHUNK) (its size in bytes:
+ * dflash_shard_stats_bytes).  With one shard per device, the columns of
+ * the other shards arrive by an exchange of these records (an all-gather,
+ * or a sum over zero-filled buffers) before dflash_verify_shards.
+ *   d            the whole problem (V = the whole vocabulary)
+ *   n_shards     1 .. DFLASH_MAX_SHARDS
+ *   shard_begin  HOST array [n_shards]: shard_begin[0] = 0, increasing, each
+ *                a multiple of 8 (bf16 logits) or 4 (fp32), below V
+ *   shard        which shard's statistics to compute, 0 .. n_shards - 1
+ *   Z_shard      [B, L + 1, width] logits of the shard (logit_dtype),
+ *                16-byte aligned
+ *   T            [B] temperatures
+ *   stats        [B, L + 1, C] x 16 bytes, written in this shard's columns
+ * One launch on `stream`; no workspace.  Invalid arguments launch nothing. */
+dflash_status dflash_shard_stats_bytes(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                       size_t* bytes);
+dflash_status dflash_shard_stats(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin, int32_t shard,
+                                 const void* Z_shard, const float* T, void* stats, void* stream);
+
+/* S6 over a vocabulary split -- dflash_verify from the statistics of every
+ * shard (dflash_shard_stats), with the residual draw's chunks restarting at
+ * every shard boundary; without a split (one shard) the outputs equal
+ * dflash_verify's, and so do they when every boundary is a multiple of
+ * DFLASH_CHUNK.  The candidates' target logits and the drawn chunk are read
+ * from the shard that holds them (one device here; across devices, only
+ * the owner of the drawn chunk would re-read it).
+ *   Z_shards     HOST array [n_shards] of device pointers, shard s's rows
+ *                [B, L + 1, width_s] (16-byte aligned)
+ *   stats        [B, L + 1, C] x 16 bytes, every shard's columns filled
+ *   the rest as dflash_verify
+ * One launch on `stream` (one block per stream); no workspace. */
+dflash_status dflash_verify_shards(const dflash_dims* d, int32_t n_shards, const int32_t* shard_begin,
+                                   const void* const* Z_shards, const void* stats, const int32_t* cand_idx,
+                                   const int32_t* path_rank, const float* q, const float* T, const uint64_t* seed,
+                                   uint64_t cycle, int32_t* accept_len, int32_t* out_tok, void* stream);
+
 /* S2 + S3 -- context gate and adjacent pair scores (P3 "A Lightweight Path
  * Selector"; P1 "A path selector").  With g_t[k] = sigmoid(sum_j
  * W_g[k,j] * h_t[j]):
@@ -322,7 +367,9 @@ enum {
   DFLASH_KERNEL_CONV2TAP = 9,       /* dflash_conv2tap */
   DFLASH_KERNEL_TRACE_VITERBI = 10, /* dflash_trace_viterbi */
   DFLASH_KERNEL_TOPK_MERGE = 11,    /* dflash_topk_merge */
-  DFLASH_KERNEL_COUNT = 12
+  DFLASH_KERNEL_SHARD_STATS = 12,   /* dflash_shard_stats */
+  DFLASH_KERNEL_SHARD_FINALIZE = 13, /* dflash_verify_shards */
+  DFLASH_KERNEL_COUNT = 14
 };
 
 /* Name of a kernel identifier ("" if out of range). */

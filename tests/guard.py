@@ -64,8 +64,9 @@ def _redraw_h(inp, b, attempt):
         inp["h"][b] = x
 
 
-def guarded(inp, streams=None, max_tries=40, guard_trace=True):
-    """Oracle results for ``streams`` with every decision clear of the guard.
+def guarded(inp, streams=None, max_tries=40, guard_trace=True, shard_begin=None):
+    """Oracle results for ``streams`` with every decision clear of the guard
+    (``shard_begin``: the vocabulary split of the residual draw's chunks).
 
     Mutates ``inp`` (seed[b] and possibly h[b]) for re-drawn streams and
     returns (results dict by stream, number of re-draws).
@@ -76,7 +77,7 @@ def guarded(inp, streams=None, max_tries=40, guard_trace=True):
     for b in streams:
         b = int(b)
         for attempt in range(max_tries):
-            r = dflash.cycle_stream(inp, b)
+            r = dflash.cycle_stream(inp, b, shard_begin=shard_begin)
             bad = violations(r["margins"], score_sensitivity(r))
             if not guard_trace:
                 bad = [x for x in bad if x[0] != "trace_gap"]
