@@ -238,6 +238,114 @@ def viterbi_leg(args, base, dfl, dv, d, ws):
             "note": "one wave per stream: L dependent max-plus steps over K x K scores"}
 
 
+def split_leg(args, base, dfl, devs, d, ws):
+    """The order a serving engine must call the path in: the select half
+    (dflash_topk, dflash_pair_scores, dflash_trace) before the target's
+    forward pass, the verify half (dflash_verify) after it.  Each half is
+    timed on its own over the rotating input sets (wall clock between two
+    synchronisations), and every launch with the library's per-launch timer;
+    the streaming launches get their roofline from their algorithmic bytes
+    (the drafter logits for the top-K, the target logits for the
+    statistics)."""
+    import torch
+    from gpu_util import alloc_outputs
+    o = alloc_outputs(base)
+    n_sets = len(devs)
+
+    def select(i):
+        dv = devs[i % n_sets]
+        dfl.dflash_topk(d, dv["U"], o["cand_idx"], o["cand_logit"], ws)
+        dfl.dflash_pair_scores(d, dv["x0"], o["cand_idx"], o["cand_logit"], dv["E"], dv["W"], dv["h"], o["S"], ws)
+        dfl.dflash_trace(d, o["S"], o["cand_idx"], dv["T"], dv["seed"], i, o["path_rank"], o["draft_tok"], o["q"])
+
+    def verify(i):
+        dv = devs[i % n_sets]
+        dfl.dflash_verify(d, dv["Z"], o["cand_idx"], o["path_rank"], o["q"], dv["T"], dv["seed"], i,
+                          o["accept_len"], o["out_tok"], ws)
+
+    res = {}
+    for name, fn in (("select_half", select), ("verify_half", verify)):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.split_steps):
+            fn(args.warmup + i)
+        torch.cuda.synchronize()
+        res[name] = {"us_per_call": round((time.perf_counter() - t0) * 1e6 / args.split_steps, 2)}
+    dfl.dflash_profile_enable(True)
+    for i in range(args.profile_steps):
+        select(i)
+        verify(i)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("topk", "gate", "scores", "trace", "stats", "finalize"):
+        n, ms = dfl.dflash_profile_collect(name)
+        if n:
+            kern[name] = round(ms * 1e3 / n, 2)
+    dfl.dflash_profile_enable(False)
+    ub, zb = logit_bytes(base)
+    ps = 2 if base["param_kind"] == "bf16" else 4
+    gate_bytes = (base["B"] * base["L"] + base["r"]) * base["hidden"] * ps
+    algo = {"topk": ub, "stats": zb, "gate": gate_bytes}
+    roof = {}
+    for k, nbytes in algo.items():
+        if k in kern:
+            gbps = nbytes / (kern[k] * 1e-6) / 1e9
+            roof[k] = {"bound": "hbm", "algorithmic_bytes": nbytes, "achieved": round(gbps, 1),
+                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    res.update({"kernel_avg_us": kern, "roofline": roof,
+                "note": "topk = both launches of dflash_topk (partial lists, then the per-row merge)"})
+    _log(f"[bench] split path: select {res['select_half']['us_per_call']} us, verify "
+         f"{res['verify_half']['us_per_call']} us; kernels " + ", ".join(f"{k}={v}us" for k, v in kern.items()))
+    return res
+
+
+def study_leg(args, dfl):
+    """Synthetic acceptance-length study (tests/study_util.py): mean accepted
+    drafts per cycle of four path selectors on planted lattices at T = 0 and
+    T = 1, every selector run through the library on all streams, and the
+    first streams of each run checked against the oracle."""
+    import numpy as np
+    import torch
+    import synth
+    from gpu_util import device_inputs, dims_of, _np_to_dev
+    from study_util import SELECTORS, guard_subset, run_gpu, variant
+    t0 = time.perf_counter()
+    inp = synth.make_lattice(0, B=args.study_streams, V=args.study_vocab, hidden=256)
+    B, L = inp["B"], inp["L"]
+    ws = dfl.workspace(dims_of(inp))
+    dev0 = device_inputs(inp)
+    zero_E = torch.zeros_like(dev0["E"])
+    subset = list(range(min(args.study_check, B)))
+    out_rec, checked, equal, dropped = {}, 0, 0, 0
+    for T in (0.0, 1.0):
+        row = {}
+        for sel in SELECTORS:
+            x = variant(inp, sel, T)
+            ref = guard_subset(x, sel, subset)
+            dropped += len(subset) - len(ref)
+            dev = dict(dev0, T=_np_to_dev(x["T"], "cuda"), seed=_np_to_dev(x["seed"], "cuda"),
+                       E=zero_E if sel == "top1" else dev0["E"])
+            acc, out = run_gpu(dfl, x, sel, ws, dev)
+            for b, (n, o) in ref.items():
+                checked += 1
+                equal += int(int(acc[b]) == int(n) and np.array_equal(out[b], o[: L + 1]))
+            row[sel] = {"mean_accepted": round(float(acc.mean()), 3),
+                        "stderr": round(float(acc.std(ddof=1) / np.sqrt(B)), 3),
+                        "tokens_per_cycle": round(float(acc.mean()) + 1.0, 3)}
+        out_rec[f"T={T:g}"] = row
+    el = time.perf_counter() - t0
+    _log("[bench] study " + "; ".join(f"{k}: " + ", ".join(f"{s} {v['mean_accepted']:.2f}" for s, v in r.items())
+                                       for k, r in out_rec.items()) + f" ({checked} oracle checks, {equal} equal)")
+    return {"workload": f"planted lattices: B={B} streams, L={L}, V={inp['V']}, K={inp['K']}, r={inp['r']}, "
+                        f"hidden=256, bf16; drafter rows x4, target mode on the planted token (p=0.8 at T=1), "
+                        f"planted tokens share one embedding direction per stream (norm 2.8)",
+            "selectors": list(SELECTORS), "results": out_rec,
+            "oracle_check": {"streams_checked": checked, "equal": equal, "dropped_near_ties": dropped},
+            "seconds": round(el, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +369,13 @@ def main():
                          "input set's logits (read ceiling)")
     ap.add_argument("--conv-steps", type=int, default=200,
                     help="timed launches of the two-tap convolution at the workload's block shape (0: skip)")
+    ap.add_argument("--split-steps", type=int, default=200,
+                    help="timed calls of each half of the split entry points (0: skip)")
+    ap.add_argument("--study-streams", type=int, default=256,
+                    help="streams of the acceptance-length study on planted lattices (0: skip)")
+    ap.add_argument("--study-vocab", type=int, default=32768, help="vocabulary of the study's lattices")
+    ap.add_argument("--study-check", type=int, default=8,
+                    help="streams of each study run checked against the oracle")
     ap.add_argument("--viterbi-steps", type=int, default=200,
                     help="timed launches of the max-sum trace on the workload's pair scores (0: skip)")
     args = ap.parse_args()
@@ -414,6 +529,9 @@ def main():
                   "us_per_cycle": round(el * 1e6 / args.steps, 2)}
         _log(f"[bench] max-sum cycle {maxsum['us_per_cycle']:.1f} us/cycle")
 
+    split = split_leg(args, base, dfl, devs, d, ws) if args.split_steps else None
+    study = study_leg(args, dfl) if args.study_streams else None
+
     logit_gbps = (ub + zb) / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -442,6 +560,8 @@ def main():
         "conv2tap": conv,
         "trace_viterbi": viterbi,
         "cycle_maxsum": maxsum,
+        "split_path": split,
+        "acceptance_study": study,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -6,4 +6,4 @@ arithmetic: it only draws random numbers, rounds them to the storage type and
 shapes planted-token structure.  See ``synth.inputs`` for the recipe.
 """
 
-from .inputs import CONFIGS, make, make_conv, bf16_bits, bf16_value  # noqa: F401
+from .inputs import CONFIGS, make, make_conv, make_lattice, bf16_bits, bf16_value  # noqa: F401

@@ -210,3 +210,54 @@ def make_conv(config_id, set_id=0, *, B=None, L=None, hidden=None, kind=None, w_
     Wt = _store(rng.standard_normal((2 * Hn, Hn), dtype=np.float32) * np.float32(w_std), pk)
     return dict(config_id=config_id, set_id=set_id, B=Bn, L=Ln, hidden=Hn, param_kind=pk, x=x, x0=x0, Wt=Wt)
 
+
+
+def make_lattice(set_id=0, *, B=256, L=8, V=151936, hidden=256, T=1.0, affinity=2.8, target_p=0.8,
+                 sharpen=4.0):
+    """Planted lattices on which the pair selector has something to find.
+
+    The drafter rows are those of the concurrent-32 recipe (a planted token
+    per position whose rank in the row follows the recall-by-position
+    figures, P1 "Sixteen candidates per position"); on top of them:
+
+    * the drafter rows are multiplied by ``sharpen`` (a power of two, so the
+      bf16 values and every rank stay exact): a drafter whose top candidates
+      stand apart, as a trained one's do, instead of the nearly flat top 16
+      of N(0, 2) rows;
+    * the target's rows 1..L put their mode on the planted token: its logit
+      is set so that at T = 1 it holds ``target_p`` of the row's mass (so at
+      T = 0 it is the row's argmax), the target "agreeing" with the planted
+      path;
+    * each stream's planted tokens and its last verified token x0 share one
+      embedding direction: E[y] = affinity * u_b (u_b a random unit vector
+      of stream b), all other rows ~ N(0, 0.02); under a gate g near 1/2
+      every consecutive pair of planted tokens then gets a bilinear bonus of
+      about affinity^2 / 2 over a pair that leaves the planted path.
+
+    Only value structure is drawn here: nothing of the method is computed.
+    Returns the input dict of ``make`` (its ``planted`` array holds the
+    planted tokens) with these Z and E.
+    """
+    inp = make(3, set_id, B=B, L=L, V=V, hidden=hidden, T=T)
+    assert sharpen > 0 and float(np.log2(sharpen)).is_integer()
+    inp["U"] = bf16_bits(bf16_value(inp["U"]) * np.float32(sharpen))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([3, set_id, 991])))
+    logit_p = np.log(target_p / (1.0 - target_p))
+    for b in range(B):
+        for t in range(L):
+            y = int(inp["planted"][b, t])
+            z = bf16_value(inp["Z"][b, t]).astype(np.float64)
+            others = np.delete(z, y)
+            mx = others.max()
+            lse = mx + np.log(np.exp(others - mx).sum())
+            inp["Z"][b, t, y] = bf16_bits(np.float32(lse + logit_p))[0]
+    r = inp["r"]
+    E = bf16_value(inp["E"]).copy()
+    for b in range(B):
+        u = rng.standard_normal(r).astype(np.float32)
+        u /= np.linalg.norm(u)
+        for tok in [int(inp["x0"][b])] + [int(y) for y in inp["planted"][b, :L]]:
+            E[tok] = np.float32(affinity) * u
+    inp["E"] = bf16_bits(E)
+    inp["name"] = "planted-lattice"
+    return inp
