@@ -40,7 +40,7 @@ __device__ __forceinline__ void gate_block(const void* __restrict__ h, const voi
   if (PT == DFLASH_BF16) {
     const int n_grp = (n_ks + kGateGroup - 1) / kGateGroup;
     const int g = gi % n_grp, tile = gi / n_grp;
-    gate_partial_bf16(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
+    gate_partial_bf16<1>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(W), R, H, r, gpart,
                       tile / gate_cols, tile - (tile / gate_cols) * gate_cols, g * kGateGroup,
                       min(kGateGroup, n_ks - g * kGateGroup), red);
   } else {

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restri
                                                         int R, int H, int r, float* __restrict__ part) {
   __shared__ float red[kGateRed];
   const int n_ks = (H + kGateSlice - 1) / kGateSlice, ks0 = blockIdx.z * kGateGroup;
-  gate_partial_bf16(h, W, R, H, r, part, blockIdx.x, blockIdx.y, ks0, min(kGateGroup, n_ks - ks0), red);
+  gate_partial_bf16<kGateGroup>(h, W, R, H, r, part, blockIdx.x, blockIdx.y, ks0, min(kGateGroup, n_ks - ks0), red);
 }
 
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
@@ -52,44 +52,83 @@ __global__ __launch_bounds__(256) void scores_kernel(const int32_t* __restrict__
   edge_contract<PT>(e, E, K, r, S + (size_t)bt * K * K);
 }
 
-// one wave per stream
-__global__ __launch_bounds__(64) void trace_kernel(const float* __restrict__ S, const int32_t* __restrict__ cand_idx,
-                                                   const float* __restrict__ T, const uint64_t* __restrict__ seed,
-                                                   uint64_t cycle, int L, int V, int K,
-                                                   int32_t* __restrict__ path_rank, int32_t* __restrict__ draft_tok,
-                                                   float* __restrict__ q) {
-  constexpr int NMAX = DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX;
-  __shared__ TraceLds tl;
-  __shared__ float Ss[NMAX];
-  __shared__ int ci[DFLASH_L_MAX * DFLASH_K_MAX];
-  const int b = blockIdx.x, lane = threadIdx.x;
+// One 1024-thread block per stream.  Every row (t, i) of the trace table
+// (position t reached from rank i) is decided up front, one 16-lane group
+// per row, by the same arithmetic the fused cycle uses (trace_row_decide),
+// so no step waits for the previous one; wave 0 then walks the table from
+// rank 0 with lane reads of the decisions held in registers, and the block
+// writes each position's rank, token and q (the row of its predecessor's
+// rank).
+constexpr int kTraceThreads = 1024;
+constexpr int kTraceRows = kTraceThreads / 16;  // table rows decided per pass
+
+__global__ __launch_bounds__(kTraceThreads) void trace_kernel(const float* __restrict__ S,
+                                                              const int32_t* __restrict__ cand_idx,
+                                                              const float* __restrict__ T,
+                                                              const uint64_t* __restrict__ seed, uint64_t cycle, int L,
+                                                              int V, int K, int32_t* __restrict__ path_rank,
+                                                              int32_t* __restrict__ draft_tok, float* __restrict__ q) {
+  constexpr int NP = DFLASH_L_MAX * DFLASH_K_MAX / kTraceRows;  // passes at most
+  __shared__ float qtab[DFLASH_L_MAX * DFLASH_K_MAX * DFLASH_K_MAX];
+  __shared__ int jst[DFLASH_L_MAX * DFLASH_K_MAX];
+  __shared__ int rank[DFLASH_L_MAX];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int lk = L * K;
   const float Tb = T[b];
-  const size_t s0 = (size_t)b * L * K * K;
-  const int n = L * K * K;
-  // every load issued before the first store; indices past the stream's
-  // arrays are clamped (a masked load would become a branch, and each
-  // branch would wait for the loads before it)
-  float sv[NMAX / 64];
-#pragma unroll
-  for (int s = 0; s < NMAX / 64; ++s) sv[s] = S[s0 + min(lane + s * 64, n - 1)];
-  int cv[DFLASH_L_MAX * DFLASH_K_MAX / 64];
-#pragma unroll
-  for (int s = 0; s < DFLASH_L_MAX * DFLASH_K_MAX / 64; ++s)
-    cv[s] = clamp_idx(cand_idx[(size_t)b * L * K + min(lane + s * 64, L * K - 1)], V);
-#pragma unroll
-  for (int s = 0; s < NMAX / 64; ++s)
-    if (lane + s * 64 < n) Ss[lane + s * 64] = sv[s];
-#pragma unroll
-  for (int s = 0; s < DFLASH_L_MAX * DFLASH_K_MAX / 64; ++s)
-    if (lane + s * 64 < L * K) ci[lane + s * 64] = cv[s];
-  trace_setup(tl, Tb, seed[b], cycle, L, lane);
-  __syncthreads();
+  const uint64_t sd = seed[b];
   const double invT = Tb > 0.0f ? 1.0 / (double)Tb : 0.0;
-  int prev = 0;
-  for (int t = 0; t < L; ++t) {
-    const size_t e0 = ((size_t)b * L + t) * K;
-    prev = trace_step_dpp(tl, &Ss[(t * K + prev) * K], Tb, invT, t, K, lane, &ci[t * K], q + e0,
-                          path_rank + (size_t)b * L + t, draft_tok + (size_t)b * L + t, nullptr);
+  const int g = tid >> 4, j = tid & 15;
+  // every load first (clamped indices, masked afterwards)
+  float sv[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * kTraceRows + g;
+    sv[p] = S[(size_t)b * lk * K + (size_t)min(row, lk - 1) * K + min(j, K - 1)];
+  }
+  const int ci = clamp_idx(cand_idx[(size_t)b * lk + min(tid, lk - 1)], V);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * kTraceRows + g;
+    if (p * kTraceRows >= lk) break;  // uniform
+    const bool live = row < lk && j < K;
+    const int t = min(row, lk - 1) / K;
+    const uint32_t u = stream_block(sd, cycle, (uint32_t)(t + 1), 0u).x;
+    float qv;
+    const int jd = trace_row_decide(sv[p], live, (tid & 63) >> 4, j, Tb, invT, u, K, qv);
+    if (live) qtab[row * K + j] = qv;
+    if (row < lk && j == 0) jst[row] = jd;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // the decisions in registers (lane l holds rows l, l + 64, ...): each
+    // step of the walk is a lane read, not an LDS round trip
+    constexpr int NJ = DFLASH_L_MAX * DFLASH_K_MAX / kWave;
+    int jv[NJ];
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) jv[c] = lane + c * kWave < lk ? jst[lane + c * kWave] : 0;
+    int prev = 0, mine = 0;
+    for (int t = 0; t < L; ++t) {
+      const int row = t * K + prev;
+      int next = 0;
+#pragma unroll
+      for (int c = 0; c < NJ; ++c) {
+        const int v = __builtin_amdgcn_readlane(jv[c], row & 63);
+        next = (row >> 6) == c ? v : next;
+      }
+      if (lane == t) mine = next;
+      prev = next;
+    }
+    if (lane < L) rank[lane] = mine;
+  }
+  __syncthreads();
+  if (tid < L) {
+    path_rank[(size_t)b * L + tid] = rank[tid];
+  }
+  if (tid < lk) {
+    const int t = tid / K, k = tid - t * K;
+    const int pr = t > 0 ? rank[t - 1] : 0;
+    q[(size_t)b * lk + tid] = qtab[(t * K + pr) * K + k];
+    if (k == rank[t]) draft_tok[(size_t)b * L + t] = ci;
   }
 }
 
@@ -125,7 +164,7 @@ hipError_t launch_scores(const dflash_dims& d, const int32_t* x0, const int32_t*
 hipError_t launch_trace(const dflash_dims& d, const float* S, const int32_t* cand_idx, const float* T,
                         const uint64_t* seed, uint64_t cycle, int32_t* path_rank, int32_t* draft_tok,
                         float* q, hipStream_t st) {
-  launch(trace_kernel, dim3((unsigned)d.B), dim3(64), st, S, cand_idx, T, seed, cycle, d.L,
+  launch(trace_kernel, dim3((unsigned)d.B), dim3(kTraceThreads), st, S, cand_idx, T, seed, cycle, d.L,
                      d.V, d.K, path_rank, draft_tok, q);
   return hipGetLastError();
 }

@@ -37,6 +37,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // B[k][n] = W_g[n][k], both contiguous along k); the accumulator holds
 // D[4 (l / 16) + i][l % 16].  A slice shorter than 256 (hidden is a
 // multiple of 16) zero-fills the 8-element groups past its end.
+// PF slices have their operand loads issued together before their MFMAs
+// (PF = 1 inside the streaming launch, whose occupancy a larger register
+// set would cut; the whole group in the standalone gate launch, which then
+// waits for one round of loads instead of one per slice).  The MFMAs run in
+// the same order for every PF, so the results are identical.
+template <int PF>
 __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                   int R, int H, int r, float* __restrict__ part, int tile_row,
                                                   int tile_col, int ks0, int n_sl, float* red) {
@@ -49,27 +55,35 @@ __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h
   v4f32 acc[kGateCT];
 #pragma unroll
   for (int ct = 0; ct < kGateCT; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
-  for (int ks = ks0; ks < ks0 + n_sl; ++ks) {
-    const int kend = min(H, ks * kGateSlice + kGateSlice);
-    const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;  // this lane's first k
-    const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
-    const uint16_t* wp = W + kw;
-    bf16x8 a[kSteps], bv[kSteps][kGateCT];
+  for (int kb = ks0; kb < ks0 + n_sl; kb += PF) {
+    bf16x8 a[PF][kSteps], bv[PF][kSteps][kGateCT];
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      const bool ok = kw + 32 * i < kend;
-      a[i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
+    for (int p = 0; p < PF; ++p) {
+      const int ks = kb + p;
+      const int kend = ks < ks0 + n_sl ? min(H, ks * kGateSlice + kGateSlice) : 0;
+      const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;  // this lane's first k
+      const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
+      const uint16_t* wp = W + kw;
 #pragma unroll
-      for (int ct = 0; ct < kGateCT; ++ct) {
-        const int c = col + ct * 16;
-        bv[i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
+      for (int i = 0; i < kSteps; ++i) {
+        const bool ok = kw + 32 * i < kend;
+        a[p][i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
+#pragma unroll
+        for (int ct = 0; ct < kGateCT; ++ct) {
+          const int c = col + ct * 16;
+          bv[p][i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i)
+    for (int p = 0; p < PF; ++p) {
+      if (kb + p >= ks0 + n_sl) break;
 #pragma unroll
-      for (int ct = 0; ct < kGateCT; ++ct)
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[i][ct], acc[ct], 0, 0, 0);
+      for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+        for (int ct = 0; ct < kGateCT; ++ct)
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[p][i], bv[p][i][ct], acc[ct], 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int ct = 0; ct < kGateCT; ++ct)
@@ -278,53 +292,6 @@ __device__ __forceinline__ float edge_contract(EdgeLds& e, const void* __restric
 
 // ---------------------------------------------------------------- trace step
 
-struct TraceLds {
-  uint32_t u[DFLASH_L_MAX];  // word 0 of the (cycle, t + 1, 0) blocks
-};
-
-__device__ __forceinline__ void trace_setup(TraceLds& tl, float Tb, uint64_t seed, uint64_t cycle, int L, int lane) {
-  if (Tb > 0.0f && lane < L) tl.u[lane] = stream_block(seed, cycle, (uint32_t)(lane + 1), 0u).x;
-}
-
-// One step of the walk by one wave; lane k < K holds the score of rank k
-// in the predecessor's row `srow` (LDS).  Greedy: smallest rank attaining
-// the maximum.  Sampling: w = exp((s - max) / T) in fp64 (the quotient
-// taken as a product with invT = 1 / T), q = w / total, and the smallest
-// rank whose inclusive prefix of w exceeds u * total.
-// `ci` (LDS) holds the clamped candidate tokens of this position.  Writes
-// q (global, and LDS when qs_lds is given), the rank and the token.
-__device__ __forceinline__ int trace_step_dpp(const TraceLds& tl, const float* srow, float Tb, double invT, int t,
-                                              int K, int lane,
-                                              const int* ci, float* __restrict__ q_out, int32_t* __restrict__ rank_out,
-                                              int32_t* __restrict__ tok_out, float* qs_lds) {
-  const float s = lane < K ? srow[lane] : -INFINITY;
-  const float m = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(row16_scan_max_f32(s)), 15));
-  int j;
-  float qv;
-  if (!(Tb > 0.0f)) {
-    j = first_lane(lane < K && s == m);
-    if (j >= K) j = 0;
-    qv = lane == j ? 1.0f : 0.0f;
-  } else {
-    const double w = lane < K ? exp_nonpos(((double)s - (double)m) * invT) : 0.0;
-    const double cum = row16_scan_f64(w);
-    const double total = readlane_f64(cum, K - 1);
-    const double target = (double)u01_f32(tl.u[t]) * total;
-    j = first_lane(lane < K && cum > target);
-    if (j >= K) j = K - 1;
-    qv = (float)(w / total);
-  }
-  if (lane < K) {
-    q_out[lane] = qv;
-    if (qs_lds) qs_lds[lane] = qv;
-  }
-  if (lane == 0) {
-    *rank_out = j;
-    *tok_out = ci[j];
-  }
-  return j;
-}
-
 // value of lane 16 g + 15 in every lane of 16-lane group g
 __device__ __forceinline__ uint32_t group_last_u32(uint32_t v, int g) {
   const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
@@ -340,14 +307,14 @@ __device__ __forceinline__ double group_last_f64(double v, int g) {
 
 // Decision of one row (t, i) of the trace table, held by a 16-lane group
 // g of the wave: lane j of the group holds s = S[t][i][j] (live: j < K),
-// the scores of the successors of rank i at position t.  The arithmetic is
-// that of trace_step_dpp: greedy, the smallest rank attaining the maximum;
-// sampling, w = exp((s - max) / T) in fp64 (as a product with invT),
-// q = w / total, and the smallest rank whose inclusive prefix of w exceeds
-// u * total, u the trace uniform (word 0 of the (cycle, t + 1, 0) block).
-// Returns the rank for every lane of the group and sets this lane's q.
-// With every row of every position decided up front, the walk itself is
-// only L table look-ups.
+// the scores of the successors of rank i at position t.  Greedy: the
+// smallest rank attaining the maximum.  Sampling: w = exp((s - max) / T) in
+// fp64 (as a product with invT = 1 / T), q = w / total, and the smallest
+// rank whose inclusive prefix of w exceeds u * total, u the trace uniform
+// (word 0 of the (cycle, t + 1, 0) block).  Returns the rank for every lane
+// of the group and sets this lane's q.  Both trace entry points (the
+// standalone trace and the fused cycle) decide every row of every position
+// up front with this function; the walk itself is then L table look-ups.
 __device__ __forceinline__ int trace_row_decide(float s, bool live, int g, int j, float Tb, double invT, uint32_t u,
                                                 int K, float& qv) {
   s = live ? s : -INFINITY;

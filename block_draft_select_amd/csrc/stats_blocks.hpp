@@ -36,28 +36,54 @@ __device__ __forceinline__ uint32_t smax_i16x2(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(s16x2, b)));
 }
 
-// Statistics of chunk c of target row `rowid` (one wave).
+// One chunk of a target row in a wave's registers: 64 raw values per lane
+// (bf16 pairs or fp32 words), lane l holding 16-byte unit j * 64 + l.
 template <int DT>
-__device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, size_t rowid, int V, int c, float Tb,
-                                                 int lane) {
-  const bool greedy = !(Tb > 0.0f);
+struct ChunkRegs {
+  uint32_t x[DT == DFLASH_BF16 ? 32 : 64];
+};
+
+// Load chunk c of target row `rowid` (one wave; nontemporal 16-byte loads).
+// 16-byte units past the row end hold -inf (weight 0, never the maximum).
+template <int DT>
+__device__ __forceinline__ void stats_load(const void* __restrict__ Z, size_t rowid, int V, int c, int lane,
+                                           ChunkRegs<DT>& r) {
   const int lo = c * kChunk, hi = min(lo + kChunk, V);
-  ChunkStat st;
-  st.pad = 0;
   if (DT == DFLASH_BF16) {
     const uint16_t* row = reinterpret_cast<const uint16_t*>(Z) + rowid * V;
-    // 16-byte units past hi hold -inf pairs (weight 0, never the maximum)
-    uint32_t x[32];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int base = lo + (j * kWave + lane) * 8;
       uint4 v = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
       if (base < hi) v = load_stream16(row + base);
-      x[4 * j + 0] = v.x;
-      x[4 * j + 1] = v.y;
-      x[4 * j + 2] = v.z;
-      x[4 * j + 3] = v.w;
+      r.x[4 * j + 0] = v.x;
+      r.x[4 * j + 1] = v.y;
+      r.x[4 * j + 2] = v.z;
+      r.x[4 * j + 3] = v.w;
     }
+  } else {
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(Z) + rowid * V;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int base = lo + (j * kWave + lane) * 4;
+      uint4 v = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+      if (base < hi) v = load_stream16(row + base);
+      r.x[4 * j + 0] = v.x;
+      r.x[4 * j + 1] = v.y;
+      r.x[4 * j + 2] = v.z;
+      r.x[4 * j + 3] = v.w;
+    }
+  }
+}
+
+// Statistics of the chunk held in r whose first token is lo (one wave).
+template <int DT>
+__device__ __forceinline__ ChunkStat stats_reduce(const ChunkRegs<DT>& r, int lo, float Tb, int lane) {
+  const bool greedy = !(Tb > 0.0f);
+  const uint32_t* x = r.x;
+  ChunkStat st;
+  st.pad = 0;
+  if (DT == DFLASH_BF16) {
     if (greedy) {
       // composite key (canonical value, inverted chunk offset): the maximum
       // is the largest value at the smallest index
@@ -112,18 +138,6 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
       st.arg = -1;
     }
   } else {
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(Z) + rowid * V;
-    uint32_t x[64];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int base = lo + (j * kWave + lane) * 4;
-      uint4 v = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
-      if (base < hi) v = load_stream16(row + base);
-      x[4 * j + 0] = v.x;
-      x[4 * j + 1] = v.y;
-      x[4 * j + 2] = v.z;
-      x[4 * j + 3] = v.w;
-    }
     if (greedy) {
       uint64_t best = 0;
 #pragma unroll
@@ -156,6 +170,15 @@ __device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, siz
     }
   }
   return st;
+}
+
+// Statistics of chunk c of target row `rowid` (one wave): load, then reduce.
+template <int DT>
+__device__ __forceinline__ ChunkStat stats_chunk(const void* __restrict__ Z, size_t rowid, int V, int c, float Tb,
+                                                 int lane) {
+  ChunkRegs<DT> r;
+  stats_load<DT>(Z, rowid, V, c, lane, r);
+  return stats_reduce<DT>(r, c * kChunk, Tb, lane);
 }
 
 template <int DT>

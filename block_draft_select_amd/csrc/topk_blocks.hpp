@@ -295,8 +295,8 @@ __device__ void merge_compact_bf16(TkWave& w, uint32_t c, int K, int lane, int l
 // returns the wave's own threshold key (the running list's K-th key + 1, or
 // the K-th largest pick); fold_bf16_scan raises it to the block bound, then
 // buffers and merges the candidates.
-__device__ __forceinline__ uint32_t fold_bf16_load(const uint16_t* __restrict__ row, int lo, int hi, int K,
-                                                   const TkWave& w, int lane, uint32_t (&x)[4 * kTopkLoads]) {
+__device__ __forceinline__ void load_sub_bf16(const uint16_t* __restrict__ row, int lo, int hi, int lane,
+                                              uint32_t (&x)[4 * kTopkLoads]) {
   // 16-byte units lie wholly inside or outside [lo, hi) (row lengths are
   // multiples of 8 values); units past hi hold 0xFFFF pairs (key 0: never
   // admitted, and a lane whose pick is padding adds nothing to the count)
@@ -310,6 +310,10 @@ __device__ __forceinline__ uint32_t fold_bf16_load(const uint16_t* __restrict__ 
     x[4 * j + 2] = v.z;
     x[4 * j + 3] = v.w;
   }
+}
+
+// the wave's threshold key for the sub-segment held in x (see above)
+__device__ __forceinline__ uint32_t sub_threshold_bf16(int K, const TkWave& w, const uint32_t (&x)[4 * kTopkLoads]) {
   const uint32_t ntop = __builtin_amdgcn_readfirstlane(w.ntop);
   uint32_t thr;
   if (ntop == (uint32_t)K) {
@@ -330,6 +334,12 @@ __device__ __forceinline__ uint32_t fold_bf16_load(const uint16_t* __restrict__ 
     if (thr == 0u) thr = 1u;            // never admit padding
   }
   return thr;
+}
+
+__device__ __forceinline__ uint32_t fold_bf16_load(const uint16_t* __restrict__ row, int lo, int hi, int K,
+                                                   const TkWave& w, int lane, uint32_t (&x)[4 * kTopkLoads]) {
+  load_sub_bf16(row, lo, hi, lane, x);
+  return sub_threshold_bf16(K, w, x);
 }
 
 __device__ __forceinline__ void fold_bf16_scan(const uint16_t* __restrict__ row, int lo, int hi, int K, TkWave& w,
