@@ -9,8 +9,8 @@
 //
 // bf16 operands: the taps are a GEMM [B*L, H] x [H, 2H] on the matrix cores
 // (v_mfma_f32_16x16x32_bf16) with the mixing fused into its epilogue, so
-// neither the taps nor a transposed copy ever reach HBM.  A block of four
-// waves (2 x 2) owns BM rows and BC channels of both taps; every 64-wide k
+// neither the taps nor a transposed copy ever reach HBM.  A block of WM x WN
+// waves owns BM rows and BC channels of both taps; every 64-wide k
 // stage of its x rows and generator rows is loaded with whole 128-byte row
 // pieces (eight lanes per row) into LDS (16-byte chunks XOR-swizzled by row,
 // so that neither the row-piece stores nor the fragment reads conflict in
@@ -32,14 +32,16 @@ namespace {
 constexpr int kConvBK = 64;                // k per LDS stage (two MFMA k-steps)
 
 // MT 16-row tiles and CT 16-channel tiles (each with both taps) per wave;
-// the block's 2 x 2 waves cover BM rows and BC channels
-template <int MT, int CT>
+// the block's WM x WN waves cover BM rows and BC channels
+template <int MT, int CT, int WM, int WN>
 struct ConvTile {
-  static constexpr int BM = 32 * MT;
-  static constexpr int BC = 32 * CT;
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int BM = 16 * MT * WM;
+  static constexpr int BC = 16 * CT * WN;
   static constexpr int ROWS = BM + 2 * BC;  // staged rows: x rows, then tap-0 and tap-1 generator rows
-  static constexpr int LOADS = ROWS * (kConvBK / 8) / 256;  // 16-byte loads per thread per stage
-  static_assert(BM % 32 == 0 && (2 * BC) % 32 == 0, "a load instruction covers 32 rows of one operand");
+  static constexpr int RPI = THREADS / 8;   // rows one load instruction covers (eight lanes per row)
+  static constexpr int LOADS = ROWS / RPI;  // 16-byte loads per thread per stage
+  static_assert(BM % RPI == 0 && (2 * BC) % RPI == 0, "a load instruction covers RPI rows of one operand");
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -66,17 +68,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int MT, int CT, int P>
-__global__ __launch_bounds__(256) void conv_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ x0,
-                                                        const uint16_t* __restrict__ Wt, int R, int L, int H, int n_rt,
-                                                        int n_ct, float* __restrict__ y) {
-  using Tl = ConvTile<MT, CT>;
+template <int MT, int CT, int P, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ x0,
+                                                                 const uint16_t* __restrict__ Wt, int R, int L, int H,
+                                                                 int n_rt, int n_ct, float* __restrict__ y) {
+  using Tl = ConvTile<MT, CT, WM, WN>;
   constexpr int PITCH = kConvBK * 2;  // 128-byte rows, 16-byte chunks XOR-swizzled by row % 8
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][Tl::ROWS * PITCH];
   int rt, ct;
   if (!conv_tile(blockIdx.x, n_rt, n_ct, rt, ct)) return;  // padding ids of the last channel group
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int row0 = rt * Tl::BM, ch0 = ct * Tl::BC;
   const int n_st = (H + kConvBK - 1) / kConvBK;
 
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(const uint16_t* __restri
   const int c8 = (tid & 7) * 8;
 #pragma unroll
   for (int i = 0; i < Tl::LOADS; ++i) {
-    const int rho = (tid >> 3) + 32 * i;
+    const int rho = (tid >> 3) + Tl::RPI * i;
     dst[i] = rho * PITCH + ((tid & 7) ^ (rho & 7)) * 16;
     if (rho < Tl::BM) {
       const int row = row0 + rho;
@@ -201,15 +204,16 @@ __global__ __launch_bounds__(256) void conv_mfma_kernel(const uint16_t* __restri
     }
 }
 
-template <int MT, int CT, int P>
+template <int MT, int CT, int P, int WM, int WN>
 hipError_t launch_conv_mfma(const void* x, const void* x0, const void* Wt, int R, int L, int H, float* y,
                             hipStream_t st) {
-  using Tl = ConvTile<MT, CT>;
+  using Tl = ConvTile<MT, CT, WM, WN>;
   const int n_rt = (R + Tl::BM - 1) / Tl::BM;
   const int n_ct = (H + Tl::BC - 1) / Tl::BC;
   const long long blocks = (long long)((n_ct + 7) / 8) * 8 * n_rt;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  launch(conv_mfma_kernel<MT, CT, P>, dim3((unsigned)blocks), dim3(256), st, reinterpret_cast<const uint16_t*>(x),
+  launch(conv_mfma_kernel<MT, CT, P, WM, WN>, dim3((unsigned)blocks), dim3(Tl::THREADS), st,
+         reinterpret_cast<const uint16_t*>(x),
          reinterpret_cast<const uint16_t*>(x0), reinterpret_cast<const uint16_t*>(Wt), R, L, H, n_rt, n_ct, y);
   return hipSuccess;
 }
@@ -261,20 +265,21 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
                            hipStream_t st) {
   const int R = d.B * d.L, H = d.hidden;
   if (d.param_dtype == DFLASH_BF16) {
-    // 128 x 64 blocks when they alone give every CU a block, else 64 x 32
     const long long big = (long long)((R + 127) / 128) * ((H + 63) / 64);
-    // P stages of loads in flight, P dividing the stage count (measured
-    // best: 4 for the 64 x 32 blocks, 2 for the 128 x 64 blocks, whose
-    // registers allow two waves per SIMD only up to that depth)
     const int n_st = (H + kConvBK - 1) / kConvBK;
+    // eight waves per block (4 x 2): 128 x 64 blocks when they alone give
+    // every CU a block (P = 2 stages of loads in flight), else 64 x 32 (P = 8);
+    // P divides the stage count (measured: 63.6 against 67.5 us at 1024 x
+    // 3072 and 17.0 against 18.7 us at 256 x 2048 for the four-wave blocks)
     hipError_t e;
     if (big >= 256) {
-      e = n_st % 2 == 0 ? launch_conv_mfma<4, 2, 2>(x, x0, Wt, R, d.L, H, y, st)
-                        : launch_conv_mfma<4, 2, 1>(x, x0, Wt, R, d.L, H, y, st);
+      e = n_st % 2 == 0 ? launch_conv_mfma<2, 2, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
+                        : launch_conv_mfma<2, 2, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     } else {
-      e = n_st % 4 == 0   ? launch_conv_mfma<2, 1, 4>(x, x0, Wt, R, d.L, H, y, st)
-          : n_st % 2 == 0 ? launch_conv_mfma<2, 1, 2>(x, x0, Wt, R, d.L, H, y, st)
-                          : launch_conv_mfma<2, 1, 1>(x, x0, Wt, R, d.L, H, y, st);
+      e = n_st % 8 == 0   ? launch_conv_mfma<1, 1, 8, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
+          : n_st % 4 == 0 ? launch_conv_mfma<1, 1, 4, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
+          : n_st % 2 == 0 ? launch_conv_mfma<1, 1, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
+                          : launch_conv_mfma<1, 1, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     }
     if (e != hipSuccess) return e;
   } else {

@@ -645,12 +645,16 @@ __device__ void finalize_stream(FinLds& f, int b, const G& geo, int L, int V, in
       const int off = (k < nk ? f.cand[ts][k] : -1) - e0;
       if (k < nk && off >= 0 && off < kFinTpt) cmask |= 1u << off;
     }
+    // the weights exp2((z - m_c) * log2(e) / T) in fp32 (v_exp_f32) of the
+    // exactly formed difference z - m_c (relative error about 2e-7),
+    // accumulated in fp64
+    const float k2 = kLog2e / Tb, mcf = (float)mc;
     double wv[kFinTpt];
     double run = 0.0;
     int last_pos = -1;
 #pragma unroll
     for (int i = 0; i < kFinTpt; ++i) {
-      const double ex = exp_nonpos((zv[i] - mc) * invT);
+      const double ex = (double)__builtin_amdgcn_exp2f(((float)zv[i] - mcf) * k2);
       const double w = (e0 + i < cl.hi && !((cmask >> i) & 1u)) ? ex : 0.0;
       if (w > 0.0) last_pos = e0 + i;
       run += w;
