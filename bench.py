@@ -205,7 +205,8 @@ def conv_leg(args, base, dfl):
         roof = {"bound": "mfma" if pk == "bf16" else "alu",
                 "achieved": round(flops / (avg_us * 1e-6) / 1e12, 1), "peak": MFMA_PEAK_TFLOPS[pk],
                 "unit": "TFLOP/s", "frac": round(t_mma / (avg_us * 1e-6), 4)}
-    roof.update({"algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops, "traffic": None})
+    roof.update({"algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops,
+                 "traffic": load_traffic("conv2tap", base["name"])})
     _log(f"[bench] conv2tap {avg_us:.2f} us/launch ({roof['frac']:.2f} of its {roof['bound']} roof)")
     return {"shape": f"B={B} L={L} hidden={H} {pk}", "launches": n, "avg_us": round(avg_us, 2),
             "wall_us_per_call": round(wall_us, 2), "generator_sets": n_sets, "roofline": roof}
