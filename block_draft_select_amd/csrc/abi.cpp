@@ -178,6 +178,7 @@ WsLayout ws_layout(const dflash_dims& d) {
   w.n_seg = (w.n_sub + w.spb - 1) / w.spb;
   w.n_chunk = (d.V + kChunk - 1) / kChunk;
   size_t o = 0;
+  w.epoch = o;        o = align256(o + sizeof(uint32_t));
   w.topk_partial = o; o = align256(o + R * w.n_seg * 16 * sizeof(uint64_t));
   w.gate = o;         o = align256(o + (size_t)gate_groups(d) * R * d.r * sizeof(float));
   w.cand_idx = o;     o = align256(o + R * d.K * sizeof(int32_t));
@@ -190,6 +191,11 @@ WsLayout ws_layout(const dflash_dims& d) {
   w.stats = o;        o = align256(o + (size_t)d.B * (d.L + 1) * w.n_chunk * sizeof(ChunkStat));
   w.jstar = o;        o = align256(o + R * d.K * sizeof(int32_t));
   w.qtab = o;         o = align256(o + R * d.K * d.K * sizeof(float));
+  w.edges = (long long)R * w.n_seg + stream_gate_blocks(d) + (long long)R <= kResidentBlocks;
+  if (w.edges) {
+    w.tk_tag = o;     o = align256(o + R * w.n_seg * 16 * 2 * sizeof(uint64_t));
+    w.gate_tag = o;   o = align256(o + (size_t)gate_groups(d) * R * d.r * sizeof(uint64_t));
+  }
   w.total = o;
   return w;
 }
@@ -469,15 +475,25 @@ static dflash_status cycle_impl(bool maxsum, const dflash_dims* d, const void* U
     int32_t* draft_tok = draft_tok_opt ? draft_tok_opt : reinterpret_cast<int32_t*>(base + w.draft_tok);
     float* q = q_opt ? q_opt : reinterpret_cast<float*>(base + w.q);
     hipStream_t st = (hipStream_t)stream;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_STREAM, st, [&] {
-          return dfk::launch_cycle_stream(*d, w, U, Z, h, W_g, T, base, st);
-        }), "stream launch")) return s;
-    if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
-          return dfk::launch_cycle_scores(*d, w, x0, E, Z, T, seed, cycle, base, cand_idx, cand_logit, S, st);
-        }), "scores launch")) return s;
+    if (w.edges) {
+      // the edges run inside the streaming launch: two launches
+      const int n_sblk = d->B * (d->L + 1) * ((w.n_chunk + 3) / 4);
+      const dfk::CycleEdges ce{(int)((long long)n_sblk * dfk::kEdgePrePct / 100), x0, E, seed, cycle, cand_idx,
+                               cand_logit, S};
+      if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_STREAM, st, [&] {
+            return dfk::launch_cycle_stream(*d, w, U, Z, h, W_g, T, base, st, &ce);
+          }), "stream launch")) return s;
+    } else {
+      if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_STREAM, st, [&] {
+            return dfk::launch_cycle_stream(*d, w, U, Z, h, W_g, T, base, st);
+          }), "stream launch")) return s;
+      if (dflash_status s = hip_status(timed(DFLASH_KERNEL_CYCLE_SCORES, st, [&] {
+            return dfk::launch_cycle_scores(*d, w, x0, E, Z, T, seed, cycle, base, cand_idx, cand_logit, S, st);
+          }), "scores launch")) return s;
+    }
     return hip_status(timed(DFLASH_KERNEL_CYCLE_FINALIZE, st, [&] {
       return dfk::launch_cycle_finalize(*d, w, Z, cand_idx, T, seed, cycle, base, maxsum ? S : nullptr, path_rank,
-                                        draft_tok, q, accept_len, out_tok, st);
+                                        draft_tok, q, accept_len, out_tok, st, w.edges);
     }), "finalize launch");
   } catch (...) {
     return fail(DFLASH_ERR_HIP, "internal error");

@@ -270,6 +270,36 @@ __host__ __device__ inline double exp_nonpos(double x) {
   return ldexp(p, (int)n);
 }
 
+// ---------------------------------------------------------------- hand-off inside a launch
+// Values passed between blocks of one launch, which may run on different
+// XCDs (each with its own L2), travel as device-scope atomic stores and
+// loads: coherent across the XCDs without a release fence (which would
+// write back a whole L2).  Nothing orders two such stores, so every entry
+// validates itself: it carries the launch's tag (odd, so a zero-filled
+// buffer never matches; an epoch that every cycle advances, so entries of
+// earlier cycles never match), and a 64-bit value split over two words
+// also carries a check word mixing value and tag (a reader that sees one
+// word new and the other old finds a mismatch and reads again).
+__device__ __forceinline__ uint32_t handoff_tag(uint32_t epoch) { return (epoch << 1) | 1u; }
+__device__ __forceinline__ uint32_t handoff_check(uint64_t v, uint32_t tag) {
+  return ((uint32_t)v * 0x9E3779B1u) ^ ((uint32_t)(v >> 32) * 0x85EBCA77u) ^ tag;
+}
+__device__ __forceinline__ void handoff_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t handoff_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// a 64-bit value with its tag and check word: words p[0], p[1]
+__device__ __forceinline__ void handoff_store_pair(uint64_t* p, uint64_t v, uint32_t tag) {
+  handoff_store(p, v);
+  handoff_store(p + 1, ((uint64_t)handoff_check(v, tag) << 32) | tag);
+}
+// a float with its tag in one word
+__device__ __forceinline__ void handoff_store_f32(uint64_t* p, float v, uint32_t tag) {
+  handoff_store(p, ((uint64_t)tag << 32) | __float_as_uint(v));
+}
+
 // ---------------------------------------------------------------- streaming loads
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 

@@ -27,6 +27,15 @@ constexpr int kTopkMaxSeg = kTopkCycleMerge / 16;
 
 constexpr int kChunk = DFLASH_CHUNK;   // target-row chunk (one wave)
 
+// 256-thread blocks of the streaming launch resident at once: eight per CU
+// on the 256 CUs of an MI355X
+constexpr int kResidentBlocks = 8 * 256;
+// statistics blocks dispatched before the edge blocks, in percent of all
+// statistics blocks (measured at concurrent-32: 41.3 to 41.9 us per cycle at
+// 30 to 40, 42.2 at 0 and at 60, 42.8 at 80; the edges then start while
+// the last top-K blocks finish)
+constexpr int kEdgePrePct = 40;
+
 // gate: the hidden dimension is cut into slices of kGateSlice; a gate block
 // accumulates kGateGroup consecutive slices of one tile on the matrix
 // cores, and consumers sum the groups' partial pre-activations W_g h in
@@ -37,6 +46,15 @@ inline int gate_slices(const dflash_dims& d) {
   return d.param_dtype == DFLASH_BF16 ? (d.hidden + kGateSlice - 1) / kGateSlice : 1;
 }
 inline int gate_groups(const dflash_dims& d) { return (gate_slices(d) + kGateGroup - 1) / kGateGroup; }
+// gate blocks of the streaming launch: bf16 tiles of 16 rows x 32 columns
+// per slice group, or one fp32 row per block
+constexpr int kGateTileRows = 16, kGateTileCols = 32;
+inline long long stream_gate_blocks(const dflash_dims& d) {
+  const long long R = (long long)d.B * d.L;
+  return d.param_dtype == DFLASH_BF16
+             ? ((R + kGateTileRows - 1) / kGateTileRows) * ((d.r + kGateTileCols - 1) / kGateTileCols) * gate_groups(d)
+             : R;
+}
 
 struct ChunkStat {
   float m;      // chunk maximum logit
@@ -52,6 +70,13 @@ struct WsLayout {
   int n_chunk;  // target chunks per row
   size_t topk_partial, gate, cand_idx, cand_logit, zc, S, path_rank, draft_tok, q, stats;
   size_t jstar, qtab;  // the fused cycle's trace table: decision and q of every row (t, i)
+  // The fused cycle runs its edges inside the streaming launch when its
+  // top-K, gate and edge blocks fit the GPU's resident blocks at once
+  // (kResidentBlocks); it then hands over through: the cycle epoch (one
+  // word, advanced by every cycle's last launch), the top-K lists as
+  // (key, check | tag) pairs and the gate partials as (tag | value) words.
+  bool edges;
+  size_t epoch, tk_tag, gate_tag;
   size_t total;
 };
 
@@ -114,15 +139,28 @@ hipError_t launch_finalize(const dflash_dims& d, const WsLayout& w, const void* 
 // dflash_cycle: (1) top-K lists + chunk statistics + gate slices,
 // (2) candidates + pair scores, (3) trace + verify
 hipError_t launch_topk_lists(const dflash_dims& d, const WsLayout& w, const void* U, char* ws, hipStream_t st);
+// the edge work folded into the streaming launch (its candidates, scores
+// and trace-table rows; zc, jstar and qtab go to the workspace)
+struct CycleEdges {
+  int n_pre;  // statistics blocks dispatched before the edge blocks
+  const int32_t* x0;
+  const void* E;
+  const uint64_t* seed;
+  uint64_t cycle;
+  int32_t* cand_idx;
+  float* cand_logit;
+  float* S;
+};
 hipError_t launch_cycle_stream(const dflash_dims& d, const WsLayout& w, const void* U, const void* Z, const void* h,
-                               const void* W_g, const float* T, char* ws, hipStream_t st);
+                               const void* W_g, const float* T, char* ws, hipStream_t st,
+                               const CycleEdges* edges = nullptr);
 hipError_t launch_cycle_scores(const dflash_dims& d, const WsLayout& w, const int32_t* x0, const void* E,
                                const void* Z, const float* T, const uint64_t* seed, uint64_t cycle, char* ws,
                                int32_t* cand_idx, float* cand_logit, float* S, hipStream_t st);
 hipError_t launch_cycle_finalize(const dflash_dims& d, const WsLayout& w, const void* Z, const int32_t* cand_idx,
                                  const float* T, const uint64_t* seed, uint64_t cycle, char* ws, const float* S_maxsum,
                                  int32_t* path_rank, int32_t* draft_tok, float* q, int32_t* accept_len,
-                                 int32_t* out_tok, hipStream_t st);
+                                 int32_t* out_tok, hipStream_t st, bool advance_epoch = false);
 hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, const void* Wt, float* y,
                            hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -19,6 +19,7 @@ typedef float v4f32 __attribute__((ext_vector_type(4)));
 constexpr int kGateWaves = 4;          // waves per gate block
 constexpr int kGateCT = 2;             // 16-column tiles per gate block (32 columns)
 constexpr int kGateCols = 16 * kGateCT;
+static_assert(kGateCols == kGateTileCols, "the host counts gate tiles of kGateTileCols columns");
 constexpr int kGateRed = kGateWaves * kGateCT * 4 * 64;  // floats of LDS per gate block
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -42,10 +43,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // set would cut; the whole group in the standalone gate launch, which then
 // waits for one round of loads instead of one per slice).  The MFMAs run in
 // the same order for every PF, so the results are identical.
+// With `tpart` set, the partials go to tpart (same indices) as hand-off
+// words (tag | value) for readers in the same launch.
 template <int PF>
 __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                   int R, int H, int r, float* __restrict__ part, int tile_row,
-                                                  int tile_col, int ks0, int n_sl, float* red) {
+                                                  int tile_col, int ks0, int n_sl, float* red,
+                                                  uint64_t* __restrict__ tpart = nullptr, uint32_t tag = 0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = tile_row * 16, col0 = tile_col * kGateCols;
   const int arow = row0 + (lane & 15);
@@ -90,7 +94,8 @@ __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((wave * kGateCT + ct) * 4 + i) * kWave + lane] = acc[ct][i];
   __syncthreads();
-  float* out = part + (size_t)(ks0 / kGateGroup) * R * r;
+  const size_t obase = (size_t)(ks0 / kGateGroup) * R * r;
+  float* out = part + obase;
 #pragma unroll
   for (int o2 = 0; o2 < kGateCT; ++o2) {
     const int o = tid + o2 * 256;
@@ -100,14 +105,18 @@ __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h
     for (int w = 0; w < kGateWaves; ++w) v += red[((w * kGateCT + ct) * 4 + i) * kWave + ln];
     const int row = row0 + (ln >> 4) * 4 + i;
     const int c = col0 + ct * 16 + (ln & 15);
-    if (row < R && c < r) out[(size_t)row * r + c] = v;
+    if (row < R && c < r) {
+      if (tpart) handoff_store_f32(tpart + obase + (size_t)row * r + c, v, tag);
+      else out[(size_t)row * r + c] = v;
+    }
   }
 }
 
 // fp32 operands: one row of pre-activations per 256-thread block, VALU
 // (a single slice)
 __device__ __forceinline__ void gate_row_f32(const float* __restrict__ h, const float* __restrict__ W, int H, int r,
-                                             float* __restrict__ part, int row) {
+                                             float* __restrict__ part, int row, uint64_t* __restrict__ tpart = nullptr,
+                                             uint32_t tag = 0) {
   const int col = threadIdx.x;
   if (col >= r) return;
   const float* hr = h + (size_t)row * H;
@@ -140,7 +149,9 @@ __device__ __forceinline__ void gate_row_f32(const float* __restrict__ h, const 
     acc[2] = fmaf(x.z, w.z, acc[2]);
     acc[3] = fmaf(x.w, w.w, acc[3]);
   }
-  part[(size_t)row * r + col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (tpart) handoff_store_f32(tpart + (size_t)row * r + col, v, tag);
+  else part[(size_t)row * r + col] = v;
 }
 
 // g = sigmoid(sum of the slice-group partials, in group order) for one

@@ -465,12 +465,14 @@ __device__ void wave_fold_f32(const uint32_t* __restrict__ row, int lo, int hi, 
 
 // The sorted top list (16 keys, zero-padded) of sub-segments
 // [seg * spb, min((seg + 1) * spb, n_sub)) of drafter row `row`, computed by
-// a 256-thread block and written to `out16` (global).  `sw` is LDS for 4
-// waves, `block_top` 16 LDS keys.
+// a 256-thread block and written to `out16` (global), or, when `out_tag` is
+// set, to out_tag as 16 hand-off pairs (key, check | tag) for readers in the
+// same launch.  `sw` is LDS for 4 waves, `block_top` 16 LDS keys.
 template <int DT>
 __device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, int K, int n_sub, int spb, int row,
                                            int seg, TkWave* sw, uint64_t* block_top, uint32_t* bbound,
-                                           uint64_t* __restrict__ out16) {
+                                           uint64_t* __restrict__ out16, uint64_t* __restrict__ out_tag = nullptr,
+                                           uint32_t tag = 0) {
   constexpr int WS = 64 * kTopkLoads * (DT == DFLASH_BF16 ? 8 : 4);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   TkWave& w = sw[wave];
@@ -519,7 +521,10 @@ __device__ __forceinline__ void topk_block(const void* __restrict__ U, int V, in
     }
   }
   __syncthreads();
-  if (tid < 16) out16[tid] = block_top[tid];
+  if (tid < 16) {
+    if (out_tag) handoff_store_pair(out_tag + 2 * tid, block_top[tid], tag);
+    else out16[tid] = block_top[tid];
+  }
 }
 
 // Merge the n_seg sorted lists of one row (global, 16 keys each) into the
