@@ -501,12 +501,17 @@ def main():
     gate_bytes = (base["B"] * base["L"] + base["r"]) * base["hidden"] * ps
     emb_bytes = base["B"] * (base["L"] * base["K"] + 1) * base["r"] * ps
     algo = {"cycle_stream": ub + zb + gate_bytes, "cycle_scores": emb_bytes}
+    if "cycle_scores" not in kern:
+        # the two-launch cycle: the candidate/score work (and its embedding
+        # reads) runs inside the streaming launch
+        algo = {"cycle_stream": ub + zb + gate_bytes + emb_bytes}
     dom = "cycle_stream"  # the HBM-bound launch
     achieved = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9 if dom in kern else None
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-            "traffic": load_traffic(dom, base["name"]), "algorithmic_bytes_per_launch": algo[dom]}
+            "traffic": load_traffic(dom, base["name"]), "algorithmic_bytes_per_launch": algo[dom],
+            "cycle_launches": 3 if "cycle_scores" in kern else 2}
     per_kernel_roof = {k: round(algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1) for k in algo if k in kern}
 
     conv = conv_leg(args, base, dfl) if args.conv_steps else None

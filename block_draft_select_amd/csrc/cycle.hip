@@ -182,7 +182,7 @@ __device__ __forceinline__ void edge_block(CandLds& cl, int bt, const uint64_t* 
       z = 0.f;
       for (int g = 0; g < n_ks; ++g) {
         const uint64_t e = handoff_load(gtag + ((size_t)g * R + bt) * r + tid);
-        ok = ok && (uint32_t)(e >> 32) == tag;
+        ok = ok && ((uint32_t)(e >> 32) ^ handoff_fmix((uint32_t)e)) == tag;
         z += __uint_as_float((uint32_t)e);
       }
     }

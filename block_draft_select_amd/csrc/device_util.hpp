@@ -275,12 +275,16 @@ __host__ __device__ inline double exp_nonpos(double x) {
 // XCDs (each with its own L2), travel as device-scope atomic stores and
 // loads: coherent across the XCDs without a release fence (which would
 // write back a whole L2).  Nothing orders two such stores, so every entry
-// validates itself: it carries the launch's tag (odd, so a zero-filled
-// buffer never matches; an epoch that every cycle advances, so entries of
-// earlier cycles never match), and a 64-bit value split over two words
-// also carries a check word mixing value and tag (a reader that sees one
-// word new and the other old finds a mismatch and reads again).
-__device__ __forceinline__ uint32_t handoff_tag(uint32_t epoch) { return (epoch << 1) | 1u; }
+// validates itself against the launch's tag: a mix of the cycle epoch,
+// which every cycle advances (so entries of earlier cycles do not match),
+// forced odd (so a zero-filled buffer never matches).  A 64-bit value split
+// over two words also carries a check word mixing value and tag (a reader
+// that sees one word new and the other old finds a mismatch and reads
+// again); a float travels in one word whose high half is the tag xor a mix
+// of the value.  Memory holding anything else passes a check by chance only
+// (about 2^-32 per entry).
+__device__ __forceinline__ uint32_t handoff_tag(uint32_t epoch) { return (epoch * 0x9E3779B1u + 0x7F4A7C15u) | 1u; }
+__device__ __forceinline__ uint32_t handoff_fmix(uint32_t bits) { return bits * 0x85EBCA77u; }
 __device__ __forceinline__ uint32_t handoff_check(uint64_t v, uint32_t tag) {
   return ((uint32_t)v * 0x9E3779B1u) ^ ((uint32_t)(v >> 32) * 0x85EBCA77u) ^ tag;
 }
@@ -295,9 +299,10 @@ __device__ __forceinline__ void handoff_store_pair(uint64_t* p, uint64_t v, uint
   handoff_store(p, v);
   handoff_store(p + 1, ((uint64_t)handoff_check(v, tag) << 32) | tag);
 }
-// a float with its tag in one word
+// a float with its tag in one word: (tag ^ fmix(value)) << 32 | value
 __device__ __forceinline__ void handoff_store_f32(uint64_t* p, float v, uint32_t tag) {
-  handoff_store(p, ((uint64_t)tag << 32) | __float_as_uint(v));
+  const uint32_t bits = __float_as_uint(v);
+  handoff_store(p, ((uint64_t)(tag ^ handoff_fmix(bits)) << 32) | bits);
 }
 
 // ---------------------------------------------------------------- streaming loads

@@ -21,7 +21,7 @@
  * through the candidate lattice, and verifies it against L+1 target logit
  * rows Z by rejection sampling (accept with min(1, p/q), resample from the
  * normalised residual max(0, p - q), bonus token when all L are accepted).
- * dflash_cycle does the whole cycle in three launches; dflash_topk,
+ * dflash_cycle does the whole cycle in two or three launches; dflash_topk,
  * dflash_pair_scores, dflash_trace and dflash_verify are its steps one by
  * one.  Beside them: dflash_trace_viterbi and dflash_cycle_maxsum take the
  * path of largest summed score instead of the greedy/sampled walk, and
@@ -36,7 +36,13 @@
  *   - Scratch lives in a caller-provided device workspace of at least
  *     dflash_workspace_bytes() bytes; its contents need no initialisation
  *     (dflash_workspace_init zero-fills one for callers who want defined
- *     contents).
+ *     contents).  The fused cycles keep one word of state in it between
+ *     calls (the epoch of the hand-off entries passed between blocks of
+ *     one launch, which validate themselves against it): memory that holds
+ *     anything other than zeros or this workspace's own earlier cycles'
+ *     entries passes that check by chance only (about 2^-32 per entry), so
+ *     zero-filling a workspace before its first fused cycle, and after it
+ *     served other sizes, rules that out.
  *     Calls that overlap in time must not share a workspace.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream).  Outputs are valid once the caller
@@ -247,7 +253,10 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
                             int32_t* out_tok, void* ws, size_t ws_bytes, void* stream);
 
 /* One whole cycle: dflash_topk, dflash_pair_scores, dflash_trace and
- * dflash_verify on one stream, with identical results, in three launches.
+ * dflash_verify on one stream, with identical results, in two launches
+ * when the candidate and score work fits inside the streaming launch (its
+ * top-K, gate and edge blocks all resident at once on the GPU: 2048
+ * 256-thread blocks on an MI355X), else in three.
  * The intermediate outputs (cand_idx [B,L,K], cand_logit [B,L,K],
  * S [B,L,K,K], path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written
  * where the caller passes non-NULL pointers and kept in the workspace
@@ -361,8 +370,9 @@ enum {
   DFLASH_KERNEL_TRACE = 3,
   DFLASH_KERNEL_STATS = 4,
   DFLASH_KERNEL_FINALIZE = 5,
-  DFLASH_KERNEL_CYCLE_STREAM = 6,   /* dflash_cycle: gate + top-K lists + target chunk statistics */
-  DFLASH_KERNEL_CYCLE_SCORES = 7,   /* dflash_cycle: candidates + pair scores */
+  DFLASH_KERNEL_CYCLE_STREAM = 6,   /* dflash_cycle: gate + top-K lists + target chunk statistics
+                                       (+ candidates and pair scores in the two-launch form) */
+  DFLASH_KERNEL_CYCLE_SCORES = 7,   /* dflash_cycle, three-launch form: candidates + pair scores */
   DFLASH_KERNEL_CYCLE_FINALIZE = 8, /* dflash_cycle: trace + verify */
   DFLASH_KERNEL_CONV2TAP = 9,       /* dflash_conv2tap */
   DFLASH_KERNEL_TRACE_VITERBI = 10, /* dflash_trace_viterbi */
