@@ -196,6 +196,9 @@ WsLayout ws_layout(const dflash_dims& d) {
     w.tk_tag = o;     o = align256(o + R * w.n_seg * 16 * 2 * sizeof(uint64_t));
     w.gate_tag = o;   o = align256(o + (size_t)gate_groups(d) * R * d.r * sizeof(uint64_t));
   }
+  w.cycle_total = o;
+  w.gate_q = o;       o = align256(o + (size_t)gate_groups(d) * (d.param_dtype == DFLASH_BF16 ? 4 : 1) * R * d.r *
+                                         sizeof(float));
   w.total = o;
   return w;
 }
@@ -271,7 +274,7 @@ dflash_status dflash_pair_scores(const dflash_dims* d, const int32_t* x0, const 
     const dfk::WsLayout w = dfk::ws_layout(*d);
     if (dflash_status s = check_ws(w, ws, ws_bytes)) return s;
     hipStream_t st = (hipStream_t)stream;
-    float* g = reinterpret_cast<float*>(static_cast<char*>(ws) + w.gate);
+    float* g = reinterpret_cast<float*>(static_cast<char*>(ws) + w.gate_q);
     if (dflash_status s = hip_status(timed(DFLASH_KERNEL_GATE, st, [&] { return dfk::launch_gate(*d, h, W_g, g, st); }), "gate launch")) return s;
     return hip_status(timed(DFLASH_KERNEL_SCORES, st, [&] {
       return dfk::launch_scores(*d, x0, cand_idx, cand_logit, E, g, S, st);
@@ -519,7 +522,8 @@ dflash_status dflash_cycle_static(const dflash_dims* d, const void* U, const voi
   try {
     g_err.clear();
     if (dflash_status s = check_dims(d)) return s;
-    const size_t need = dfk::ws_layout(*d).total;
+    // the cycle's own regions (the split path's tail is not touched)
+    const size_t need = dfk::ws_layout(*d).cycle_total;
     if (need > DFLASH_STATIC_SCRATCH_BYTES)
       return fail(DFLASH_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
                                             " bytes of scratch, above the static maximum of " +

@@ -77,6 +77,10 @@ struct WsLayout {
   // (key, check | tag) pairs and the gate partials as (tag | value) words.
   bool edges;
   size_t epoch, tk_tag, gate_tag;
+  size_t cycle_total;  // bytes the fused cycles use (the regions above)
+  // the split path's gate partials, one per quarter of each tile (bf16
+  // parameters) or one per row (fp32), after everything the cycles use
+  size_t gate_q;
   size_t total;
 };
 

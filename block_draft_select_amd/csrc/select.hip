@@ -10,11 +10,15 @@ namespace dfk {
 namespace {
 
 // grid (row tiles, column tiles, groups of hidden slices)
-__global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                        int R, int H, int r, float* __restrict__ part) {
-  __shared__ float red[kGateRed];
-  const int n_ks = (H + kGateSlice - 1) / kGateSlice, ks0 = blockIdx.z * kGateGroup;
-  gate_partial_bf16<kGateGroup>(h, W, R, H, r, part, blockIdx.x, blockIdx.y, ks0, min(kGateGroup, n_ks - ks0), red);
+// one wave per quarter of a tile (grid z = group * 4 + quarter): a tile's
+// 192 KB of operands spread over four CUs instead of one, the whole group's
+// loads of the quarter issued before its first MFMA; the consumer sums the
+// quarters as the cycle's four-wave tiles do, so the scores are identical
+__global__ __launch_bounds__(64) void gate_mfma_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                       int R, int H, int r, float* __restrict__ qpart) {
+  const int n_ks = (H + kGateSlice - 1) / kGateSlice, ks0 = (blockIdx.z / kGateWaves) * kGateGroup;
+  gate_quarter_bf16<kGateGroup>(h, W, R, H, r, qpart, blockIdx.x, blockIdx.y, ks0, min(kGateGroup, n_ks - ks0),
+                                blockIdx.z % kGateWaves);
 }
 
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ h, const float* __restrict__ W,
@@ -47,7 +51,11 @@ __global__ __launch_bounds__(256) void scores_kernel(const int32_t* __restrict__
     e.cidx[tid] = c;
     e.cl[tid] = cl;
   }
-  edge_gate(e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
+  if (PT == DFLASH_BF16) {
+    if (tid < r) e.g[tid] = gate_value_quarters(gpart, n_ks, (size_t)gridDim.x * r, bt, r, tid);
+  } else {
+    edge_gate(e, gpart, n_ks, (size_t)gridDim.x * r, bt, r);
+  }
   __syncthreads();
   edge_contract<PT>(e, E, K, r, S + (size_t)bt * K * K);
 }
@@ -137,8 +145,9 @@ __global__ __launch_bounds__(kTraceThreads) void trace_kernel(const float* __res
 hipError_t launch_gate(const dflash_dims& d, const void* h, const void* W_g, float* gpart, hipStream_t st) {
   const int R = d.B * d.L;
   if (d.param_dtype == DFLASH_BF16) {
-    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols), (unsigned)gate_groups(d));
-    launch(gate_mfma_kernel, grid, dim3(256), st, reinterpret_cast<const uint16_t*>(h),
+    const dim3 grid((unsigned)((R + 15) / 16), (unsigned)((d.r + kGateCols - 1) / kGateCols),
+                    (unsigned)(gate_groups(d) * kGateWaves));
+    launch(gate_mfma_kernel, grid, dim3(64), st, reinterpret_cast<const uint16_t*>(h),
                        reinterpret_cast<const uint16_t*>(W_g), R, d.hidden, d.r, gpart);
   } else {
     launch(gate_f32_kernel, dim3((unsigned)R), dim3(256), st, reinterpret_cast<const float*>(h),

@@ -40,9 +40,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // multiple of 16) zero-fills the 8-element groups past its end.
 // PF slices have their operand loads issued together before their MFMAs
 // (PF = 1 inside the streaming launch, whose occupancy a larger register
-// set would cut; the whole group in the standalone gate launch, which then
-// waits for one round of loads instead of one per slice).  The MFMAs run in
-// the same order for every PF, so the results are identical.
+// set would cut).  The MFMAs run in the same order for every PF, so the
+// results are identical; gate_quarter_bf16 below computes the same chains
+// one wave per block for the standalone gate.
 // With `tpart` set, the partials go to tpart (same indices) as hand-off
 // words (tag | value) for readers in the same launch.
 template <int PF>
@@ -110,6 +110,83 @@ __device__ __forceinline__ void gate_partial_bf16(const uint16_t* __restrict__ h
       else out[(size_t)row * r + c] = v;
     }
   }
+}
+
+// One quarter of gate_partial_bf16's tile in a block of one wave: the
+// MFMA chain of quarter q (k in [64 q, 64 q + 64) of every slice of the
+// group), written to qpart[grp][q][row][col] unsummed; the consumer adds the
+// four quarters in order (0 + q0 + q1 + q2 + q3), which is the sum the
+// four-wave tile forms in LDS, so the results are identical.
+template <int PF>
+__device__ __forceinline__ void gate_quarter_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                  int R, int H, int r, float* __restrict__ qpart, int tile_row,
+                                                  int tile_col, int ks0, int n_sl, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = tile_row * 16, col0 = tile_col * kGateCols;
+  const int arow = row0 + (lane & 15);
+  const int col = col0 + (lane & 15);
+  constexpr int kSteps = kGateSlice / kGateWaves / 32;
+  const bf16x8 zero = {};
+  v4f32 acc[kGateCT];
+#pragma unroll
+  for (int ct = 0; ct < kGateCT; ++ct) acc[ct] = (v4f32){0.f, 0.f, 0.f, 0.f};
+  for (int kb = ks0; kb < ks0 + n_sl; kb += PF) {
+    bf16x8 a[PF][kSteps], bv[PF][kSteps][kGateCT];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int ks = kb + p;
+      const int kend = ks < ks0 + n_sl ? min(H, ks * kGateSlice + kGateSlice) : 0;
+      const int kw = ks * kGateSlice + wave * (kGateSlice / kGateWaves) + (lane >> 4) * 8;
+      const uint16_t* hp = h + (size_t)min(arow, R - 1) * H + kw;
+      const uint16_t* wp = W + kw;
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        const bool ok = kw + 32 * i < kend;
+        a[p][i] = ok && arow < R ? *reinterpret_cast<const bf16x8*>(hp + 32 * i) : zero;
+#pragma unroll
+        for (int ct = 0; ct < kGateCT; ++ct) {
+          const int c = col + ct * 16;
+          bv[p][i][ct] = ok && c < r ? *reinterpret_cast<const bf16x8*>(wp + (size_t)c * H + 32 * i) : zero;
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (kb + p >= ks0 + n_sl) break;
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+        for (int ct = 0; ct < kGateCT; ++ct)
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[p][i], bv[p][i][ct], acc[ct], 0, 0, 0);
+    }
+  }
+  float* out = qpart + ((size_t)(ks0 / kGateGroup) * kGateWaves + wave) * R * r;
+#pragma unroll
+  for (int ct = 0; ct < kGateCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + (lane >> 4) * 4 + i;
+      const int c = col0 + ct * 16 + (lane & 15);
+      if (row < R && c < r) out[(size_t)row * r + c] = acc[ct][i];
+    }
+}
+
+// g from the quarters: per group (0 + q0 + q1 + q2 + q3), the groups added
+// in order, then the sigmoid (the same sums as gate_value over the tiles)
+__device__ __forceinline__ float gate_value_quarters(const float* __restrict__ qpart, int n_grp, size_t stride, int row,
+                                                     int r, int col) {
+  const float* p = qpart + (size_t)row * r + col;
+  float z = 0.f;
+  for (int g = 0; g < n_grp; ++g) {
+    float v[kGateWaves];
+#pragma unroll
+    for (int q = 0; q < kGateWaves; ++q) v[q] = p[((size_t)g * kGateWaves + q) * stride];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kGateWaves; ++q) s += v[q];
+    z += s;
+  }
+  return 1.0f / (1.0f + expf(-z));
 }
 
 // fp32 operands: one row of pre-activations per 256-thread block, VALU

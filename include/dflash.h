@@ -275,10 +275,11 @@ dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
  * own file-scope device array of DFLASH_STATIC_SCRATCH_BYTES (8 MiB) per
  * GPU, held until the process ends; no call allocates or frees anything.
  * Same arguments, results and launches as dflash_cycle otherwise.
- *   - Sizes whose workspace (dflash_workspace_bytes) exceeds
- *     DFLASH_STATIC_SCRATCH_BYTES are rejected with DFLASH_ERR_WORKSPACE
- *     before anything is enqueued (the five benchmark shapes, up to
- *     B = 128, L = 8, V = 262144, need at most 5.7 MiB).
+ *   - Sizes whose cycle workspace (dflash_workspace_bytes less the split
+ *     path's gate partials, which the layout keeps last and the cycle does
+ *     not touch) exceeds DFLASH_STATIC_SCRATCH_BYTES are rejected with
+ *     DFLASH_ERR_WORKSPACE before anything is enqueued (the five benchmark
+ *     shapes, up to B = 128, L = 8, V = 262144, need at most 5.7 MiB).
  *   - The first call on a device looks up the array's device address with
  *     hipGetSymbolAddress (a host-side query, no allocation) while that
  *     device is current; make that first call outside graph capture.
