@@ -260,7 +260,11 @@ dflash_status dflash_verify(const dflash_dims* d, const void* Z, const int32_t* 
  * The intermediate outputs (cand_idx [B,L,K], cand_logit [B,L,K],
  * S [B,L,K,K], path_rank [B,L], draft_tok [B,L], q [B,L,K]) are written
  * where the caller passes non-NULL pointers and kept in the workspace
- * otherwise. */
+ * otherwise.
+ * The call enqueues kernels only (no allocation, copy or memset), so it may
+ * be captured into a HIP graph: a replay repeats the captured arguments,
+ * the cycle number included, while the workspace's hand-off epoch, device
+ * state that every cycle advances, keeps successive replays apart. */
 dflash_status dflash_cycle(const dflash_dims* d, const void* U, const void* Z,
                            const int32_t* x0, const void* E, const void* W_g, const void* h,
                            const float* T, const uint64_t* seed, uint64_t cycle,
@@ -295,9 +299,10 @@ dflash_status dflash_cycle_static(const dflash_dims* d, const void* U, const voi
                                   void* stream);
 
 /* The whole cycle with the max-sum trace (dflash_trace_viterbi) in place of
- * the greedy/sampled walk, in three launches like dflash_cycle: its
- * streaming and candidate/score launches, then one block per stream that
- * finds the max-sum path over the pair scores and runs the verify.  Same
+ * the greedy/sampled walk, in two or three launches like dflash_cycle: its
+ * streaming launch (with the candidate/score work inside when it fits, else
+ * a candidate/score launch after it), then one block per stream that finds
+ * the max-sum path over the pair scores and runs the verify.  Same
  * arguments, layouts and workspace as dflash_cycle; q is one-hot.  Outputs
  * equal those of dflash_topk, dflash_pair_scores, dflash_trace_viterbi and
  * dflash_verify called in turn. */
