@@ -156,6 +156,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t*
         for (int tap = 0; tap < 2; ++tap)
           b[ks][c][tap] = *reinterpret_cast<const bf16x8*>(st + (b_row + tap * Tl::BC + c * 16) * PITCH + fo[ks]);
     }
+    // one-tile waves: left to itself the scheduler hangs each MFMA behind
+    // its own fragment read's LDS round trip; the scheduling barrier keeps
+    // the stage's reads together ahead of the MFMAs (measured 16.0 to 16.3
+    // against 17.1 to 17.7 us at 256 x 2048; the larger tiles interleave
+    // well by themselves and measured slower with it)
+    if constexpr (MT == 1 && CT == 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kConvBK / 32; ++ks)
 #pragma unroll
@@ -266,13 +272,21 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
   const int R = d.B * d.L, H = d.hidden;
   if (d.param_dtype == DFLASH_BF16) {
     const long long big = (long long)((R + 127) / 128) * ((H + 63) / 64);
+    const long long wide = (long long)((R + 127) / 128) * ((H + 95) / 96);
     const int n_st = (H + kConvBK - 1) / kConvBK;
-    // eight waves per block (4 x 2): 128 x 64 blocks when they alone give
-    // every CU a block (P = 2 stages of loads in flight), else 64 x 32 (P = 8);
-    // P divides the stage count (measured: 63.6 against 67.5 us at 1024 x
-    // 3072 and 17.0 against 18.7 us at 256 x 2048 for the four-wave blocks)
+    // eight waves per block (4 x 2), P dividing the stage count.  128 x 96
+    // blocks (P = 4, else 2) when they give 7/8 to all of the CUs one block
+    // each: their registers leave one block per CU, and they stage the
+    // fewest bytes per CU (55 to 56 against 62 to 63 us for 128 x 64 at
+    // 1024 x 3072).  Else 128 x 64 blocks (P = 2; two fit a CU) when they
+    // alone give every CU a block, else 64 x 32 (P = 8).  Eight waves
+    // against four of the same tile: 63.6 against 67.5 us at 1024 x 3072,
+    // 17.0 against 18.7 us at 256 x 2048.
     hipError_t e;
-    if (big >= 256) {
+    if (wide >= 224 && wide <= 256 && n_st % 2 == 0) {
+      e = n_st % 4 == 0 ? launch_conv_mfma<2, 3, 4, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
+                        : launch_conv_mfma<2, 3, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
+    } else if (big >= 256) {
       e = n_st % 2 == 0 ? launch_conv_mfma<2, 2, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
                         : launch_conv_mfma<2, 2, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     } else {

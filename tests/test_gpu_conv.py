@@ -81,6 +81,12 @@ CASES = [
     ("bf16-one-row-min-hidden", 3, dict(B=1, L=1, hidden=16), None),
     ("bf16-wide-hidden", 3, dict(B=2, L=2, hidden=4096), None),
     ("bf16-large-tiles-ragged", 3, dict(B=100, L=5, hidden=4112), [0, 51, 99]),
+    # the 128 x 96 tiles (one block per CU): ragged rows (936 = 7 * 128 +
+    # 40), channels (2800 = 29 * 96 + 16) and k (2800 = 43 * 64 + 48) with
+    # four stages of loads in flight; then 960 rows, 2944 channels (30 * 96
+    # + 64) and 46 stages, two in flight
+    ("bf16-wide-tiles-ragged", 3, dict(B=117, L=8, hidden=2800), [0, 58, 116]),
+    ("bf16-wide-tiles-two-stages", 3, dict(B=120, L=8, hidden=2944), [0, 119]),
 ]
 
 
