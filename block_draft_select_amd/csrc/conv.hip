@@ -11,11 +11,12 @@
 // (v_mfma_f32_16x16x32_bf16) with the mixing fused into its epilogue, so
 // neither the taps nor a transposed copy ever reach HBM.  A block of WM x WN
 // waves owns BM rows and BC channels of both taps; every 64-wide k
-// stage of its x rows and generator rows is loaded with whole 128-byte row
-// pieces (eight lanes per row) into LDS (16-byte chunks XOR-swizzled by row,
-// so that neither the row-piece stores nor the fragment reads conflict in
-// the banks), double-buffered, with P stages of loads in flight in
-// registers while the MFMAs read the current one.  A wave owns MT row tiles and CT channel tiles of both taps,
+// stage of its x rows and generator rows lands in LDS as whole 128-byte row
+// pieces (16-byte chunks XOR-swizzled by row, so that neither the stores
+// nor the fragment reads conflict in the banks), either straight from
+// global memory into a ring of stage buffers (global_load_lds_dwordx4) or
+// through registers into a double buffer with P stages of loads in flight,
+// while the MFMAs read the current stage.  A wave owns MT row tiles and CT channel tiles of both taps,
 // so the two taps of each output sit in the same lane and the epilogue
 // mixes them from registers.  The row tiles of one channel tile share an XCD (block id mod 8), so that
 // tile's generator rows come from HBM once and from that XCD's L2 after.
@@ -40,8 +41,7 @@ struct ConvTile {
   static constexpr int BC = 16 * CT * WN;
   static constexpr int ROWS = BM + 2 * BC;  // staged rows: x rows, then tap-0 and tap-1 generator rows
   static constexpr int RPI = THREADS / 8;   // rows one load instruction covers (eight lanes per row)
-  static constexpr int LOADS = ROWS / RPI;  // 16-byte loads per thread per stage
-  static_assert(BM % RPI == 0 && (2 * BC) % RPI == 0, "a load instruction covers RPI rows of one operand");
+  static constexpr int LOADS = ROWS / RPI;  // 16-byte loads per thread per stage (register-staged ring)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -68,6 +68,79 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// MFMA fragment offsets inside a stage: lane row lane % 16 (tile rows start
+// at multiples of 16, so the row's swizzle key is lane % 8), 16-byte chunk
+// 4 * ks + lane / 16 of the 64-wide stage
+struct ConvFrag {
+  int fo[kConvBK / 32];
+  __device__ __forceinline__ explicit ConvFrag(int lane) {
+#pragma unroll
+    for (int ks = 0; ks < kConvBK / 32; ++ks) {
+      const int c = 4 * ks + (lane >> 4);
+      fo[ks] = (lane & 15) * (kConvBK * 2) + (c ^ (lane & 7)) * 16;
+    }
+  }
+};
+
+// one stage's MFMAs of a wave: every fragment first, then the products
+template <int MT, int CT, int BC>
+__device__ __forceinline__ void conv_stage(const unsigned char* st, const ConvFrag& f, int a_row, int b_row,
+                                           v4f32 (&acc)[MT][CT][2]) {
+  constexpr int PITCH = kConvBK * 2;
+  bf16x8 a[kConvBK / 32][MT], b[kConvBK / 32][CT][2];
+#pragma unroll
+  for (int ks = 0; ks < kConvBK / 32; ++ks) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a[ks][m] = *reinterpret_cast<const bf16x8*>(st + (a_row + m * 16) * PITCH + f.fo[ks]);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int tap = 0; tap < 2; ++tap)
+        b[ks][c][tap] = *reinterpret_cast<const bf16x8*>(st + (b_row + tap * BC + c * 16) * PITCH + f.fo[ks]);
+  }
+  // one-tile waves: left to itself the scheduler hangs each MFMA behind its
+  // own fragment read's LDS round trip; the scheduling barrier keeps the
+  // stage's reads together ahead of the MFMAs (16.0 to 16.3 against 17.1 to
+  // 17.7 us at 256 x 2048; the larger tiles interleave well by themselves)
+  if constexpr (MT == 1 && CT == 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < kConvBK / 32; ++ks)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int tap = 0; tap < 2; ++tap)
+          acc[m][c][tap] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][m], b[ks][c][tap], acc[m][c][tap], 0, 0, 0);
+}
+
+// epilogue: element e of the lane holds (row 4 * (lane / 16) + e, channel
+// lane % 16) of each tile; both taps of that output are in this lane
+template <int MT, int CT>
+__device__ __forceinline__ void conv_mix_store(const v4f32 (&acc)[MT][CT][2], const uint16_t* __restrict__ x,
+                                               const uint16_t* __restrict__ x0, int R, int L, int H, int rbase,
+                                               int cbase, int lane, float* __restrict__ y) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int ch = cbase + c * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + m * 16 + 4 * (lane >> 4) + e;
+        if (row >= R || ch >= H) continue;
+        const int t = row % L;
+        const float xv = bf16_to_f32(x[(size_t)row * H + ch]);
+        const float xp = bf16_to_f32(t > 0 ? x[(size_t)(row - 1) * H + ch] : x0[(size_t)(row / L) * H + ch]);
+        y[(size_t)row * H + ch] = fmaf(acc[m][c][1][e], xp, acc[m][c][0][e] * xv);
+      }
+    }
+}
+
+// Register-staged ring: each thread loads its LOADS row pieces of a stage
+// into registers (P stages in flight) and stores them to a double-buffered
+// LDS.  Used for the 128 x 64 tiles, whose 64 KB of LDS lets two blocks
+// share a CU.
 template <int MT, int CT, int P, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ x0,
@@ -75,6 +148,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t*
                                                                  int n_rt, int n_ct, float* __restrict__ y) {
   using Tl = ConvTile<MT, CT, WM, WN>;
   constexpr int PITCH = kConvBK * 2;  // 128-byte rows, 16-byte chunks XOR-swizzled by row % 8
+  static_assert(Tl::BM % Tl::RPI == 0 && (2 * Tl::BC) % Tl::RPI == 0, "a load instruction covers rows of one operand");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][Tl::ROWS * PITCH];
   int rt, ct;
   if (!conv_tile(blockIdx.x, n_rt, n_ct, rt, ct)) return;  // padding ids of the last channel group
@@ -111,15 +185,14 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t*
   // compiler would then wait for every load in flight before each store):
   // a k run past the row end reads the row's last eight values instead,
   // and the store writes zeros for it and for rows past the edge
-  auto stage_k = [&](int s) { return s * kConvBK; };
   auto load_stage = [&](int s, uint4(&r)[Tl::LOADS]) {
-    const int k0 = stage_k(s);
+    const int k0 = s * kConvBK;
     const int ko = k0 + c8 < H ? k0 : H - 8 - c8;
 #pragma unroll
     for (int i = 0; i < Tl::LOADS; ++i) r[i] = *reinterpret_cast<const uint4*>(src[i] + ko);
   };
   auto store_stage = [&](const uint4(&r)[Tl::LOADS], int s, int buf) {
-    const unsigned kok = stage_k(s) + c8 < H ? 0xFFFFFFFFu : 0u;
+    const unsigned kok = s * kConvBK + c8 < H ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < Tl::LOADS; ++i) {
       const unsigned m = kok & rmask[i];
@@ -132,46 +205,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t*
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[m][c][0] = acc[m][c][1] = (v4f32){0.f, 0.f, 0.f, 0.f};
-  // fragment offsets: lane row lane % 16 (tile rows start at multiples of
-  // 16, so the row's swizzle key is lane % 8), 16-byte chunk
-  // 4 * ks + lane / 16 of the 64-wide stage
-  int fo[kConvBK / 32];
-#pragma unroll
-  for (int ks = 0; ks < kConvBK / 32; ++ks) {
-    const int c = 4 * ks + (lane >> 4);
-    fo[ks] = (lane & 15) * PITCH + (c ^ (lane & 7)) * 16;
-  }
+  const ConvFrag f(lane);
   const int a_row = wm * 16 * MT, b_row = Tl::BM + wn * 16 * CT;
-  auto compute = [&](const unsigned char* st) {
-    // every fragment of the stage first, then the MFMAs
-    bf16x8 a[kConvBK / 32][MT], b[kConvBK / 32][CT][2];
-#pragma unroll
-    for (int ks = 0; ks < kConvBK / 32; ++ks) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        a[ks][m] = *reinterpret_cast<const bf16x8*>(st + (a_row + m * 16) * PITCH + fo[ks]);
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int tap = 0; tap < 2; ++tap)
-          b[ks][c][tap] = *reinterpret_cast<const bf16x8*>(st + (b_row + tap * Tl::BC + c * 16) * PITCH + fo[ks]);
-    }
-    // one-tile waves: left to itself the scheduler hangs each MFMA behind
-    // its own fragment read's LDS round trip; the scheduling barrier keeps
-    // the stage's reads together ahead of the MFMAs (measured 16.0 to 16.3
-    // against 17.1 to 17.7 us at 256 x 2048; the larger tiles interleave
-    // well by themselves and measured slower with it)
-    if constexpr (MT == 1 && CT == 1) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < kConvBK / 32; ++ks)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-          for (int tap = 0; tap < 2; ++tap)
-            acc[m][c][tap] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][m], b[ks][c][tap], acc[m][c][tap], 0, 0, 0);
-  };
 
   // straight-line ring (P divides the stage count, so no stage test inside
   // the unrolled body): the last P stages reload the final stage into slots
@@ -185,29 +220,113 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_mfma_kernel(const uint16_t*
     for (int u = 0; u < P; ++u) {
       const int s = s0 + u;
       load_stage(min(s + P, n_st - 1), pre[u]);  // stage s is in LDS already
-      compute(lds[s & 1]);
+      conv_stage<MT, CT, Tl::BC>(lds[s & 1], f, a_row, b_row, acc);
       store_stage(pre[(u + 1) % P], min(s + 1, n_st - 1), (s + 1) & 1);
       lds_barrier();
     }
   }
+  conv_mix_store<MT, CT>(acc, x, x0, R, L, H, row0 + wm * 16 * MT, ch0 + wn * 16 * CT, lane, y);
+}
 
-  // epilogue: element e of the lane holds (row 4 * (lane / 16) + e, channel
-  // lane % 16) of each tile; both taps of that output are in this lane
+// One 16-byte piece per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's piece lands at l * 16 bytes past the
+// wave-uniform LDS address.  The data never passes through registers, and
+// the wave's vmcnt counts the transfer.  The host pass of the kernel
+// templates does not know the builtin, so it is compiled in the device pass
+// only.
+__device__ __forceinline__ void load_to_lds16(const uint16_t* g, unsigned char* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
+
+// Direct-to-LDS ring: NB stage buffers, stages s + 1 .. s + NB - 2 in flight
+// while stage s is multiplied, one barrier per stage.  A wave instruction
+// fills one 8-row group of a stage (8 x 128 bytes, contiguous in LDS): lane
+// l writes row 8g + l / 8 at position l % 8, which holds the row's chunk
+// (l % 8) ^ (l / 8), so the swizzle is applied on the global side.  Rows
+// past the edge read a clamped row: they only feed outputs that are never
+// stored.  A k run past the row end reads the row's last eight values, and
+// the stage holding it is cleared there before it is used.
+template <int MT, int CT, int NB, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ x0,
+                                                                const uint16_t* __restrict__ Wt, int R, int L, int H,
+                                                                int n_rt, int n_ct, float* __restrict__ y) {
+  using Tl = ConvTile<MT, CT, WM, WN>;
+  constexpr int NW = WM * WN;
+  constexpr int PITCH = kConvBK * 2;
+  constexpr int GROUPS = Tl::ROWS / 8;  // 8-row groups per stage
+  constexpr int LPW = GROUPS / NW;      // load instructions per wave per stage
+  constexpr int INFLIGHT = LPW * (NB - 2);
+  static_assert(GROUPS % NW == 0, "whole groups per wave");
+  static_assert(NB >= 3 && INFLIGHT <= 63, "a stage multiplied, one landing, the vmcnt field");
+  constexpr int SBYTES = Tl::ROWS * PITCH;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * SBYTES];
+  int rt, ct;
+  if (!conv_tile(blockIdx.x, n_rt, n_ct, rt, ct)) return;  // padding ids of the last channel group
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave % WM, wn = wave / WM;
+  const int row0 = rt * Tl::BM, ch0 = ct * Tl::BC;
+  const int n_st = (H + kConvBK - 1) / kConvBK;
+
+  // group g = wave + NW * i of every stage is this wave's instruction i
+  const uint16_t* rowp[LPW];
+  const int cc = ((lane & 7) ^ (lane >> 3)) * 8;  // element column of the lane's chunk
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int rho = 8 * (wave + NW * i) + (lane >> 3);
+    if (rho < Tl::BM) {
+      rowp[i] = x + (size_t)min(row0 + rho, R - 1) * H;
+    } else {
+      const int j = rho - Tl::BM, tap = j / Tl::BC, c = ch0 + j - tap * Tl::BC;
+      rowp[i] = Wt + ((size_t)tap * H + min(c, H - 1)) * H;
+    }
+  }
+  auto issue = [&](int s) {
+    const int col = min(s * kConvBK + cc, H - 8);
+    unsigned char* base = lds + (s % NB) * SBYTES;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) load_to_lds16(rowp[i] + col, base + (wave + NW * i) * (8 * PITCH));
+  };
+
+  v4f32 acc[MT][CT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int ch = ch0 + wn * 16 * CT + c * 16 + (lane & 15);
+    for (int c = 0; c < CT; ++c) acc[m][c][0] = acc[m][c][1] = (v4f32){0.f, 0.f, 0.f, 0.f};
+  const ConvFrag f(lane);
+  const int a_row = wm * 16 * MT, b_row = Tl::BM + wn * 16 * CT;
+
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = row0 + wm * 16 * MT + m * 16 + 4 * (lane >> 4) + e;
-        if (row >= R || ch >= H) continue;
-        const int t = row % L;
-        const float xv = bf16_to_f32(x[(size_t)row * H + ch]);
-        const float xp = bf16_to_f32(t > 0 ? x[(size_t)(row - 1) * H + ch] : x0[(size_t)(row / L) * H + ch]);
-        y[(size_t)row * H + ch] = fmaf(acc[m][c][1][e], xp, acc[m][c][0][e] * xv);
-      }
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < n_st) issue(u);
+  for (int s = 0; s < n_st; ++s) {
+    // this wave's transfers of stage s are done when at most those of the
+    // stages issued after it (s + 1 .. min(s + NB - 2, n_st - 1)) remain;
+    // the barrier then makes the whole stage visible, and tells every wave
+    // that all have finished reading the buffer stage s - 1 used
+    asm volatile("" ::: "memory");
+    if (s + NB - 2 <= n_st - 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14));  // vmcnt(INFLIGHT)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    unsigned char* st = lds + (s % NB) * SBYTES;
+    if (s * kConvBK + kConvBK > H) {
+      const int valid = (H - s * kConvBK) / 8;  // whole chunks inside the row (hidden % 16 == 0)
+      for (int q = tid; q < Tl::ROWS * 8; q += 64 * NW) {
+        const int r = q >> 3, pos = q & 7;
+        if ((pos ^ (r & 7)) >= valid) *reinterpret_cast<uint4*>(st + r * PITCH + pos * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      lds_barrier();
+    }
+    if (s + NB - 1 < n_st) issue(s + NB - 1);  // into the buffer stage s - 1 used
+    conv_stage<MT, CT, Tl::BC>(st, f, a_row, b_row, acc);
+  }
+  conv_mix_store<MT, CT>(acc, x, x0, R, L, H, row0 + wm * 16 * MT, ch0 + wn * 16 * CT, lane, y);
 }
 
 template <int MT, int CT, int P, int WM, int WN>
@@ -219,8 +338,22 @@ hipError_t launch_conv_mfma(const void* x, const void* x0, const void* Wt, int R
   const long long blocks = (long long)((n_ct + 7) / 8) * 8 * n_rt;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   launch(conv_mfma_kernel<MT, CT, P, WM, WN>, dim3((unsigned)blocks), dim3(Tl::THREADS), st,
-         reinterpret_cast<const uint16_t*>(x),
-         reinterpret_cast<const uint16_t*>(x0), reinterpret_cast<const uint16_t*>(Wt), R, L, H, n_rt, n_ct, y);
+         reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(x0),
+         reinterpret_cast<const uint16_t*>(Wt), R, L, H, n_rt, n_ct, y);
+  return hipSuccess;
+}
+
+template <int MT, int CT, int NB, int WM, int WN>
+hipError_t launch_conv_lds(const void* x, const void* x0, const void* Wt, int R, int L, int H, float* y,
+                           hipStream_t st) {
+  using Tl = ConvTile<MT, CT, WM, WN>;
+  const int n_rt = (R + Tl::BM - 1) / Tl::BM;
+  const int n_ct = (H + Tl::BC - 1) / Tl::BC;
+  const long long blocks = (long long)((n_ct + 7) / 8) * 8 * n_rt;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  launch(conv_lds_kernel<MT, CT, NB, WM, WN>, dim3((unsigned)blocks), dim3(Tl::THREADS), st,
+         reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(x0),
+         reinterpret_cast<const uint16_t*>(Wt), R, L, H, n_rt, n_ct, y);
   return hipSuccess;
 }
 
@@ -274,26 +407,24 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
     const long long big = (long long)((R + 127) / 128) * ((H + 63) / 64);
     const long long wide = (long long)((R + 127) / 128) * ((H + 95) / 96);
     const int n_st = (H + kConvBK - 1) / kConvBK;
-    // eight waves per block (4 x 2), P dividing the stage count.  128 x 96
-    // blocks (P = 4, else 2) when they give 7/8 to all of the CUs one block
-    // each: their registers leave one block per CU, and they stage the
-    // fewest bytes per CU (55 to 56 against 62 to 63 us for 128 x 64 at
-    // 1024 x 3072).  Else 128 x 64 blocks (P = 2; two fit a CU) when they
-    // alone give every CU a block, else 64 x 32 (P = 8).  Eight waves
-    // against four of the same tile: 63.6 against 67.5 us at 1024 x 3072,
-    // 17.0 against 18.7 us at 256 x 2048.
+    // eight waves per block (4 x 2).  128 x 96 tiles when they give 7/8 to
+    // all of the CUs one block each (they stage the fewest bytes per CU),
+    // direct to LDS with three stage buffers (120 KB).  Else 128 x 64 tiles
+    // when they alone give every CU a block, register-staged with P = 2
+    // stages in flight (P divides the stage count), so that two blocks fit
+    // a CU.  Else 64 x 32 tiles direct to LDS with four buffers (64 KB).
+    // Measured at 1024 x 3072: 55 us for the 128 x 96 tiles direct to LDS,
+    // 56 to 57 register-staged (P = 4), 62 to 63 for 128 x 64; at 256 x
+    // 2048: 14.5 to 15.0 us for the 64 x 32 tiles direct to LDS, 15.6 to
+    // 16.3 register-staged.
     hipError_t e;
-    if (wide >= 224 && wide <= 256 && n_st % 2 == 0) {
-      e = n_st % 4 == 0 ? launch_conv_mfma<2, 3, 4, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
-                        : launch_conv_mfma<2, 3, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
+    if (wide >= 224 && wide <= 256) {
+      e = launch_conv_lds<2, 3, 3, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     } else if (big >= 256) {
       e = n_st % 2 == 0 ? launch_conv_mfma<2, 2, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
                         : launch_conv_mfma<2, 2, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     } else {
-      e = n_st % 8 == 0   ? launch_conv_mfma<1, 1, 8, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
-          : n_st % 4 == 0 ? launch_conv_mfma<1, 1, 4, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
-          : n_st % 2 == 0 ? launch_conv_mfma<1, 1, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
-                          : launch_conv_mfma<1, 1, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
+      e = launch_conv_lds<1, 1, 4, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
     }
     if (e != hipSuccess) return e;
   } else {

@@ -75,18 +75,20 @@ CASES = [
     ("bf16-concurrent-32", 3, dict(), None),                       # B 32, L 8, hidden 2048
     ("bf16-large-vocab-128", 5, dict(), [0, 77, 127]),              # B 128, L 8, hidden 3072
     # limits: one row at the smallest hidden; a wide hidden on the small
-    # tiles; the large tiles with ragged rows (500 = 3 * 128 + 116), ragged
-    # channels (4112 = 64 * 64 + 16) and an odd stage count (one stage of
-    # loads in flight)
+    # tiles; the 128 x 64 tiles with ragged rows (500 = 3 * 128 + 116),
+    # ragged channels (4112 = 64 * 64 + 16) and an odd stage count (one stage
+    # of loads in flight)
     ("bf16-one-row-min-hidden", 3, dict(B=1, L=1, hidden=16), None),
     ("bf16-wide-hidden", 3, dict(B=2, L=2, hidden=4096), None),
     ("bf16-large-tiles-ragged", 3, dict(B=100, L=5, hidden=4112), [0, 51, 99]),
-    # the 128 x 96 tiles (one block per CU): ragged rows (936 = 7 * 128 +
-    # 40), channels (2800 = 29 * 96 + 16) and k (2800 = 43 * 64 + 48) with
-    # four stages of loads in flight; then 960 rows, 2944 channels (30 * 96
-    # + 64) and 46 stages, two in flight
+    # the 128 x 96 tiles (one block per CU, direct to LDS): ragged rows
+    # (936 = 7 * 128 + 40), channels (2800 = 29 * 96 + 16) and k (2800 =
+    # 43 * 64 + 48, the last stage cleared past the row end); then 960 rows
+    # and 2944 channels (30 * 96 + 64) with whole stages
     ("bf16-wide-tiles-ragged", 3, dict(B=117, L=8, hidden=2800), [0, 58, 116]),
-    ("bf16-wide-tiles-two-stages", 3, dict(B=120, L=8, hidden=2944), [0, 119]),
+    ("bf16-wide-tiles-whole-stages", 3, dict(B=120, L=8, hidden=2944), [0, 119]),
+    # the 128 x 64 tiles with two stages of loads in flight in registers
+    ("bf16-large-tiles-two-stages", 3, dict(B=128, L=8, hidden=2048), [0, 64, 127]),
 ]
 
 
