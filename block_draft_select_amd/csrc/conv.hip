@@ -240,8 +240,9 @@ __device__ __forceinline__ void load_to_lds16(const uint16_t* g, unsigned char* 
 #endif
 }
 
-// Direct-to-LDS ring: NB stage buffers, stages s + 1 .. s + NB - 2 in flight
-// while stage s is multiplied, one barrier per stage.  A wave instruction
+// Direct-to-LDS ring: NB stage buffers, one barrier per stage; while stage
+// s is multiplied, stages s + 1 .. s + NB - 2 are in flight, and stage
+// s + NB - 1 is issued after its MFMAs into the buffer stage s - 1 used.  A wave instruction
 // fills one 8-row group of a stage (8 x 128 bytes, contiguous in LDS): lane
 // l writes row 8g + l / 8 at position l % 8, which holds the row's chunk
 // (l % 8) ^ (l / 8), so the swizzle is applied on the global side.  Rows
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
   constexpr int LPW = GROUPS / NW;      // load instructions per wave per stage
   constexpr int INFLIGHT = LPW * (NB - 2);
   static_assert(GROUPS % NW == 0, "whole groups per wave");
-  static_assert(NB >= 3 && INFLIGHT <= 63, "a stage multiplied, one landing, the vmcnt field");
+  static_assert(NB >= 3 && INFLIGHT <= 63, "a stage multiplied, one refilling, one landing; the vmcnt field");
   constexpr int SBYTES = Tl::ROWS * PITCH;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * SBYTES];
   int rt, ct;
@@ -283,9 +284,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
       rowp[i] = Wt + ((size_t)tap * H + min(c, H - 1)) * H;
     }
   }
-  auto issue = [&](int s) {
-    const int col = min(s * kConvBK + cc, H - 8);
-    unsigned char* base = lds + (s % NB) * SBYTES;
+  // stage t into buffer t % NB; past the last stage the last one is loaded
+  // again into a buffer no later stage uses, so that every wave issues the
+  // same count and the waits below hold at the tail too
+  auto issue = [&](int t) {
+    const int col = min(min(t, n_st - 1) * kConvBK + cc, H - 8);
+    unsigned char* base = lds + (t % NB) * SBYTES;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) load_to_lds16(rowp[i] + col, base + (wave + NW * i) * (8 * PITCH));
   };
@@ -299,19 +303,14 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
   const int a_row = wm * 16 * MT, b_row = Tl::BM + wn * 16 * CT;
 
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (u < n_st) issue(u);
+  for (int u = 0; u < NB - 1; ++u) issue(u);
   for (int s = 0; s < n_st; ++s) {
-    // this wave's transfers of stage s are done when at most those of the
-    // stages issued after it (s + 1 .. min(s + NB - 2, n_st - 1)) remain;
-    // the barrier then makes the whole stage visible, and tells every wave
-    // that all have finished reading the buffer stage s - 1 used
+    // this wave's transfers of stage s are done when only those of the
+    // NB - 2 stages issued after it remain, and its LDS reads are done; the
+    // barrier then makes the whole stage visible and tells every wave that
+    // all have finished reading the buffer that stage s - 1 used
     asm volatile("" ::: "memory");
-    if (s + NB - 2 <= n_st - 1) {
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14));  // vmcnt(INFLIGHT)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
+    __builtin_amdgcn_s_waitcnt(0x0070 | (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14));  // vmcnt(INFLIGHT) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     unsigned char* st = lds + (s % NB) * SBYTES;
@@ -323,9 +322,13 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
       }
       lds_barrier();
     }
-    if (s + NB - 1 < n_st) issue(s + NB - 1);  // into the buffer stage s - 1 used
     conv_stage<MT, CT, Tl::BC>(st, f, a_row, b_row, acc);
+    // stage s + NB - 1 into the buffer stage s - 1 used, issued after this
+    // stage's fragment reads so that the wave's MFMAs are not queued behind
+    // the transfers (50 against 55 us at 1024 x 3072 issued before them)
+    issue(s + NB - 1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no transfer outlives the loop
   conv_mix_store<MT, CT>(acc, x, x0, R, L, H, row0 + wm * 16 * MT, ch0 + wn * 16 * CT, lane, y);
 }
 
@@ -413,7 +416,7 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
     // when they alone give every CU a block, register-staged with P = 2
     // stages in flight (P divides the stage count), so that two blocks fit
     // a CU.  Else 64 x 32 tiles direct to LDS with four buffers (64 KB).
-    // Measured at 1024 x 3072: 55 us for the 128 x 96 tiles direct to LDS,
+    // Measured at 1024 x 3072: 50 us for the 128 x 96 tiles direct to LDS,
     // 56 to 57 register-staged (P = 4), 62 to 63 for 128 x 64; at 256 x
     // 2048: 14.5 to 15.0 us for the 64 x 32 tiles direct to LDS, 15.6 to
     // 16.3 register-staged.
