@@ -258,9 +258,10 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
   constexpr int NW = WM * WN;
   constexpr int PITCH = kConvBK * 2;
   constexpr int GROUPS = Tl::ROWS / 8;  // 8-row groups per stage
-  constexpr int LPW = GROUPS / NW;      // load instructions per wave per stage
-  constexpr int INFLIGHT = LPW * (NB - 2);
-  static_assert(GROUPS % NW == 0, "whole groups per wave");
+  // load instructions per wave per stage: group g = wave + NW * i is the
+  // wave's instruction i, so the first GROUPS % NW waves take one more
+  constexpr int LPW = (GROUPS + NW - 1) / NW, LPW_LO = GROUPS / NW, NHI = GROUPS % NW;
+  constexpr int INFLIGHT = LPW * (NB - 2), INFLIGHT_LO = LPW_LO * (NB - 2);
   static_assert(NB >= 3 && INFLIGHT <= 63, "a stage multiplied, one refilling, one landing; the vmcnt field");
   constexpr int SBYTES = Tl::ROWS * PITCH;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * SBYTES];
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
   const int cc = ((lane & 7) ^ (lane >> 3)) * 8;  // element column of the lane's chunk
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int rho = 8 * (wave + NW * i) + (lane >> 3);
+    const int rho = min(8 * (wave + NW * i) + (lane >> 3), Tl::ROWS - 1);  // past the groups: unused
     if (rho < Tl::BM) {
       rowp[i] = x + (size_t)min(row0 + rho, R - 1) * H;
     } else {
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
     const int col = min(min(t, n_st - 1) * kConvBK + cc, H - 8);
     unsigned char* base = lds + (t % NB) * SBYTES;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load_to_lds16(rowp[i] + col, base + (wave + NW * i) * (8 * PITCH));
+    for (int i = 0; i < LPW; ++i)
+      if (wave + NW * i < GROUPS) load_to_lds16(rowp[i] + col, base + (wave + NW * i) * (8 * PITCH));
   };
 
   v4f32 acc[MT][CT][2];
@@ -305,12 +307,15 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds_kernel(const uint16_t* 
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) issue(u);
   for (int s = 0; s < n_st; ++s) {
-    // this wave's transfers of stage s are done when only those of the
-    // NB - 2 stages issued after it remain, and its LDS reads are done; the
+    // this wave's transfers of stage s are done when only its transfers of
+    // the NB - 2 stages issued after it remain, and its LDS reads are done; the
     // barrier then makes the whole stage visible and tells every wave that
     // all have finished reading the buffer that stage s - 1 used
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0x0070 | (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14));  // vmcnt(INFLIGHT) lgkmcnt(0)
+    if (NHI == 0 || wave < NHI)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (INFLIGHT & 15) | ((INFLIGHT >> 4) << 14));  // vmcnt(INFLIGHT) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070 | (INFLIGHT_LO & 15) | ((INFLIGHT_LO >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     unsigned char* st = lds + (s % NB) * SBYTES;
@@ -410,19 +415,20 @@ hipError_t launch_conv2tap(const dflash_dims& d, const void* x, const void* x0, 
     const long long big = (long long)((R + 127) / 128) * ((H + 63) / 64);
     const long long wide = (long long)((R + 127) / 128) * ((H + 95) / 96);
     const int n_st = (H + kConvBK - 1) / kConvBK;
-    // eight waves per block (4 x 2).  128 x 96 tiles when they give 7/8 to
-    // all of the CUs one block each (they stage the fewest bytes per CU),
-    // direct to LDS with three stage buffers (120 KB).  Else 128 x 64 tiles
-    // when they alone give every CU a block, register-staged with P = 2
-    // stages in flight (P divides the stage count), so that two blocks fit
-    // a CU.  Else 64 x 32 tiles direct to LDS with four buffers (64 KB).
-    // Measured at 1024 x 3072: 50 us for the 128 x 96 tiles direct to LDS,
-    // 56 to 57 register-staged (P = 4), 62 to 63 for 128 x 64; at 256 x
-    // 2048: 14.5 to 15.0 us for the 64 x 32 tiles direct to LDS, 15.6 to
-    // 16.3 register-staged.
+    // 128 x 96 tiles when they give 7/8 to all of the CUs one block each
+    // (they stage the fewest bytes per CU), twelve waves (4 x 3) direct to
+    // LDS with three stage buffers (120 KB).  Else 128 x 64 tiles when
+    // they alone give every CU a block, eight waves (4 x 2) register-staged
+    // with P = 2 stages in flight (P divides the stage count), so that two
+    // blocks fit a CU.  Else 64 x 32 tiles, eight waves direct to LDS with
+    // four buffers (64 KB).  Measured at 1024 x 3072: 50.4 us for the
+    // 128 x 96 tiles direct to LDS (51.8 with eight waves), 56 to 57
+    // register-staged (P = 4), 62 to 63 for 128 x 64; at 256 x 2048: 14.5
+    // to 15.0 us for the 64 x 32 tiles direct to LDS, 15.6 to 16.3
+    // register-staged.
     hipError_t e;
     if (wide >= 224 && wide <= 256) {
-      e = launch_conv_lds<2, 3, 3, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
+      e = launch_conv_lds<2, 2, 3, 4, 3>(x, x0, Wt, R, d.L, H, y, st);
     } else if (big >= 256) {
       e = n_st % 2 == 0 ? launch_conv_mfma<2, 2, 2, 4, 2>(x, x0, Wt, R, d.L, H, y, st)
                         : launch_conv_mfma<2, 2, 1, 4, 2>(x, x0, Wt, R, d.L, H, y, st);
