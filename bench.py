@@ -377,6 +377,8 @@ def main():
     ap.add_argument("--study-vocab", type=int, default=32768, help="vocabulary of the study's lattices")
     ap.add_argument("--study-check", type=int, default=8,
                     help="streams of each study run checked against the oracle")
+    ap.add_argument("--graph-cycles", type=int, default=20,
+                    help="cycles captured into one HIP graph for the replay leg (0: skip)")
     ap.add_argument("--viterbi-steps", type=int, default=200,
                     help="timed launches of the max-sum trace on the workload's pair scores (0: skip)")
     args = ap.parse_args()
@@ -455,6 +457,40 @@ def main():
     pct = lambda f: per[min(len(per) - 1, int(f * (len(per) - 1) + 0.5))]
     cycle_us = {"p10": round(pct(0.1), 2), "median": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
     _log(f"[bench] cycle time p10/median/p90 {cycle_us['p10']}/{cycle_us['median']}/{cycle_us['p90']} us")
+
+    # the same cycles replayed from a captured HIP graph: graph_cycles
+    # consecutive cycles over the rotating sets captured once, the graph
+    # replayed; the launches are the eager path's, but a replay repeats the
+    # captured cycle numbers, so this times the launch path only (the
+    # draws repeat) and `value` stays the eager rate
+    graph = None
+    if args.graph_cycles:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(args.graph_cycles):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.graph_cycles):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // args.graph_cycles)
+        tg = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_us = (time.perf_counter() - tg) * 1e6 / (reps * args.graph_cycles)
+        graph = {"us_per_cycle": round(g_us, 2), "cycles_per_s": round(1e6 / g_us, 1),
+                 "cycles_per_graph": args.graph_cycles, "replays": reps,
+                 "note": "launch path only: a replay repeats the captured cycle numbers"}
+        del g
+        _log(f"[bench] graph replay {g_us:.1f} us/cycle ({args.graph_cycles} cycles per graph)")
 
     # per-kernel durations: HIP events recorded by the library around each
     # launch on the stream it launches on
@@ -548,6 +584,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "cycle_us": cycle_us,
+        "graph_replay": graph,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
