@@ -111,3 +111,39 @@ def test_conv2tap_identity_generator_squares():
     y = _run(inp)
     x = O.widen(inp["x"], "bf16")
     np.testing.assert_array_equal(y, x * x)
+
+
+@pytest.mark.parametrize("kw", [dict(B=4, L=8, hidden=256), dict(B=117, L=8, hidden=2800),
+                                dict(B=128, L=8, hidden=2048)],
+                         ids=["small-tiles", "wide-tiles", "register-ring"])
+def test_conv2tap_graph_replay_equals_eager(kw):
+    # the call enqueues one kernel and nothing else, so a caller may capture
+    # it into a HIP graph; every replay must give the eager call's y exactly
+    # (one tiling per case: 64 x 32 and 128 x 96 direct to LDS, 128 x 64
+    # register-staged)
+    import torch
+    import block_draft_select_amd as dfl
+    inp = synth.make_conv(3, set_id=6, **kw)
+    B, L, H = inp["B"], inp["L"], inp["hidden"]
+    _say(f"[conv] graph replay: B={B} L={L} hidden={H}")
+    d = dfl.dims(B, L, 64, 16, 16, H, "bf16", "bf16")
+    x, x0, Wt = (_np_to_dev(inp[k], "cuda") for k in ("x", "x0", "Wt"))
+    y_ref = torch.empty((B, L, H), dtype=torch.float32, device="cuda")
+    dfl.dflash_conv2tap(d, x, x0, Wt, y_ref)
+    y = torch.empty_like(y_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dfl.dflash_conv2tap(d, x, x0, Wt, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dfl.dflash_conv2tap(d, x, x0, Wt, y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep} differs from the eager call"
