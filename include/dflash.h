@@ -348,9 +348,10 @@ dflash_status dflash_trace_viterbi(const dflash_dims* d, const float* S, const i
  *   Wt  [2*hidden, hidden] param_dtype, 16-byte aligned: row c generates
  *       w0[c], row hidden + c generates w1[c] (k contiguous per tap)
  *   y   [B, L, hidden]   fp32, written
- * Caller-owned device buffers; one launch on `stream`; no workspace.  fp32
- * accumulation (bf16 products are exact in fp32).  Invalid arguments launch
- * nothing and leave y untouched. */
+ * Caller-owned device buffers; one launch on `stream` (kernels only, so the
+ * call may be captured into a HIP graph); no workspace.  fp32 accumulation
+ * (bf16 products are exact in fp32) in a fixed order, so repeated calls give
+ * identical y.  Invalid arguments launch nothing and leave y untouched. */
 dflash_status dflash_conv2tap(const dflash_dims* d, const void* x, const void* x0, const void* Wt, float* y,
                               void* stream);
 
