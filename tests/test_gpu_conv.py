@@ -89,6 +89,11 @@ CASES = [
     ("bf16-wide-tiles-whole-stages", 3, dict(B=120, L=8, hidden=2944), [0, 119]),
     # the 128 x 64 tiles with two stages of loads in flight in registers
     ("bf16-large-tiles-two-stages", 3, dict(B=128, L=8, hidden=2048), [0, 64, 127]),
+    # the smallest hidden on the large tilings (many rows): channel tiles
+    # wider than hidden, one stage with a k tail; 32768 rows take the
+    # 128 x 96 tiles, 40960 the 128 x 64 register-staged ones
+    ("bf16-wide-tiles-min-hidden", 3, dict(B=2048, L=16, hidden=16), [0, 1023, 2047]),
+    ("bf16-large-tiles-min-hidden", 3, dict(B=2560, L=16, hidden=16), [0, 1279, 2559]),
 ]
 
 
